@@ -1,0 +1,250 @@
+/*
+ * ckv_oracle.c -- plain, slow, fp64 CPU oracle of the CommunityKV decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file; only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark do.  It shares no code, header, table or helper with the HIP library.
+ *
+ * Sources (the method is described only in prose; no listing exists):
+ *   [RIT-graph]   rit.work post "CommunityKV long-context decoding", section
+ *                 "Граф токенов заменяет повторную кластеризацию" (the token graph
+ *                 replaces repeated clustering).
+ *   [RIT-granul]  same post, section "Ускорение зависит от того, сколько графов
+ *                 хранит модель" (speed-up depends on how many graphs are kept).
+ *   [ABSTRACT]    "CommunityKV: Efficient Long-Context Decoding via Graph
+ *                 Partitioning" (McKenna, Alexandridis, Susanj, Liu, 2026), abstract.
+ *
+ * Per graph and decode step the method (a) compares the query only with the
+ * community centres, (b) keeps communities under a small token budget, (c) always
+ * adds the initial sink tokens, (d) computes exact attention over the chosen
+ * tokens of the full cache and (e) attaches the new token to one neighbouring
+ * community and moves that single centre [RIT-graph; ABSTRACT].  The pages leave
+ * the score formula, the fill rule, the tie-break, "neighbouring" and the
+ * precision open; the readings taken here are stated at each function.
+ *
+ * Arithmetic: every sum, product, exponential and quotient is fp64, compiled with
+ * -ffp-contract=off so each operation rounds once, in source order.  Inputs are
+ * the stored bytes (bf16 or fp32) widened exactly to fp64.  Two values are kept
+ * in fp32 because they are fp32 state of the method: the per-community score used
+ * for ordering, and the centroid (fp64 update, rounded once per update).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define CKVO_DT_F32 0
+#define CKVO_DT_BF16 1
+
+/* Widen element i of a bf16 or fp32 array to fp64 (exact in both cases). */
+static double widen(const void *p, long i, int dtype)
+{
+    if (dtype == CKVO_DT_BF16) {
+        uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float *)p)[i];
+}
+
+/*
+ * Centroid score of one graph [RIT-graph: the decode query is compared with the
+ * community centres only; RIT-granul: one graph can serve a group of heads].
+ * Reading: the score of community c is the largest, over the graph's query heads
+ * h, of the inner product q_h . mu_c, times `scale` (1/sqrt(d)), in fp64; it is
+ * then stored as fp32.  Empty communities (size 0) score -inf.
+ *
+ *   q      : G query rows of d elements, row h at q + h*d  (dtype q_dtype)
+ *   cent   : C rows of d fp32, row c at cent + c*d
+ *   size   : C community sizes
+ *   out    : C fp32 scores
+ */
+void ckvo_score(int d, int G, const void *q, int q_dtype, const float *cent,
+                const int32_t *size, int C, float scale, float *out)
+{
+    for (int c = 0; c < C; ++c) {
+        if (size[c] <= 0) {
+            out[c] = -INFINITY;
+            continue;
+        }
+        double best = -INFINITY;
+        for (int h = 0; h < G; ++h) {
+            double dot = 0.0;
+            for (int i = 0; i < d; ++i)
+                dot = dot + widen(q, (long)h * d + i, q_dtype) * (double)cent[(long)c * d + i];
+            if (dot > best)
+                best = dot;
+        }
+        out[c] = (float)(best * (double)scale);
+    }
+}
+
+/* Order used for selection: higher score first, lower community id on equal score. */
+typedef struct {
+    float s;
+    int c;
+} ckvo_item;
+
+static int item_cmp(const void *a, const void *b)
+{
+    const ckvo_item *x = (const ckvo_item *)a, *y = (const ckvo_item *)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->c < y->c) ? -1 : (x->c > y->c);
+}
+
+/*
+ * Budgeted community selection and update candidates for one graph
+ * [RIT-granul: a small active token budget; RIT-graph: chosen communities are
+ * loaded whole].  Reading: sort the non-empty communities by (score desc, id asc);
+ * keep the longest prefix of that order whose sizes sum to at most `budget`
+ * (sinks are not counted); stop at the first community that does not fit.
+ * The first min(M, #non-empty) communities of the same order are the
+ * "neighbouring" communities offered to the local update.
+ *
+ *   sel   : C flags, 1 = selected            cand : up to M community ids
+ *   returns k* (number selected); *n_cand gets the number of candidates.
+ */
+int ckvo_select(int C, const float *score, const int32_t *size, int budget, int M,
+                uint8_t *sel, int32_t *cand, int *n_cand)
+{
+    ckvo_item *it = (ckvo_item *)malloc(sizeof(ckvo_item) * (size_t)(C > 0 ? C : 1));
+    int m = 0;
+    for (int c = 0; c < C; ++c) {
+        sel[c] = 0;
+        if (size[c] > 0) {
+            it[m].s = score[c];
+            it[m].c = c;
+            ++m;
+        }
+    }
+    qsort(it, (size_t)m, sizeof(ckvo_item), item_cmp);
+    long total = 0;
+    int k = 0;
+    while (k < m && total + size[it[k].c] <= (long)budget) {
+        total += size[it[k].c];
+        sel[it[k].c] = 1;
+        ++k;
+    }
+    int nc = m < M ? m : M;
+    for (int i = 0; i < nc; ++i)
+        cand[i] = it[i].c;
+    *n_cand = nc;
+    free(it);
+    return k;
+}
+
+/*
+ * Token index list of one graph [RIT-graph: the initial sink tokens are kept out
+ * of the graph and always added; the chosen communities are then read from the
+ * cache].  Reading: positions 0..min(S,n)-1 first, then the members of every
+ * selected community in ascending community id, each in stored member order.
+ * Returns the list length.
+ */
+int ckvo_index_list(int n, int S, int C, const uint8_t *sel, const int32_t *start,
+                    const int32_t *size, const int32_t *members, int32_t *idx)
+{
+    int len = 0;
+    int ns = S < n ? S : n;
+    for (int j = 0; j < ns; ++j)
+        idx[len++] = j;
+    for (int c = 0; c < C; ++c) {
+        if (!sel[c])
+            continue;
+        for (int j = 0; j < size[c]; ++j)
+            idx[len++] = members[start[c] + j];
+    }
+    return len;
+}
+
+/*
+ * Exact softmax attention of one query head over the listed tokens [RIT-graph:
+ * exact attention inside the reduced token set, read from the full cache].
+ *   z_j = (q . K_j) * scale,   o = sum_j exp(z_j - max z) V_j / sum_j exp(z_j - max z)
+ * K and V rows: element i of token j at K + j*row_stride + i.  An empty list
+ * gives o = 0.
+ */
+void ckvo_attend(int d, const void *q, int q_dtype, const void *K, const void *V,
+                 int kv_dtype, long row_stride, const int32_t *idx, int len,
+                 float scale, double *out)
+{
+    for (int i = 0; i < d; ++i)
+        out[i] = 0.0;
+    if (len <= 0)
+        return;
+    double *z = (double *)malloc(sizeof(double) * (size_t)len);
+    double zmax = -INFINITY;
+    for (int t = 0; t < len; ++t) {
+        long row = (long)idx[t] * row_stride;
+        double dot = 0.0;
+        for (int i = 0; i < d; ++i)
+            dot = dot + widen(q, i, q_dtype) * widen(K, row + i, kv_dtype);
+        z[t] = dot * (double)scale;
+        if (z[t] > zmax)
+            zmax = z[t];
+    }
+    double denom = 0.0;
+    for (int t = 0; t < len; ++t) {
+        double w = exp(z[t] - zmax);
+        long row = (long)idx[t] * row_stride;
+        denom = denom + w;
+        for (int i = 0; i < d; ++i)
+            out[i] = out[i] + w * widen(V, row + i, kv_dtype);
+    }
+    for (int i = 0; i < d; ++i)
+        out[i] = out[i] / denom;
+    free(z);
+}
+
+/*
+ * Local update of one graph for the new token at position n [RIT-graph: the new
+ * token is attached to a suitable neighbouring community and only that centre is
+ * updated, at a cost set by the model dimension and not by the context length;
+ * ABSTRACT: constant-time local update rule].
+ * Reading: among the candidate communities pick the one whose centroid is nearest
+ * to k_new in squared L2 (fp64; lower id on equal distance), append n to its
+ * member list, grow its size by one and move its centroid to the running mean
+ *   mu <- fp32( mu + (k_new - mu) / size_new )        (fp64 arithmetic).
+ * Returns the chosen id, or -1 when that community is full (nothing changes),
+ * or -2 when there are no candidates.  *madds counts the multiply-adds done.
+ */
+int ckvo_update(int d, const void *k_new, int dtype, const int32_t *cand, int n_cand,
+                float *cent, int32_t *size, const int32_t *cap, const int32_t *start,
+                int32_t *members, int n, long *madds)
+{
+    long ops = 0;
+    int best = -1;
+    double best_d = INFINITY;
+    for (int m = 0; m < n_cand; ++m) {
+        int c = cand[m];
+        double dist = 0.0;
+        for (int i = 0; i < d; ++i) {
+            double diff = widen(k_new, i, dtype) - (double)cent[(long)c * d + i];
+            dist = dist + diff * diff;
+            ++ops;
+        }
+        if (dist < best_d || (dist == best_d && c < best)) {
+            best_d = dist;
+            best = c;
+        }
+    }
+    if (madds)
+        *madds = ops;
+    if (best < 0)
+        return -2;
+    if (size[best] >= cap[best])
+        return -1;
+    members[start[best] + size[best]] = n;
+    size[best] += 1;
+    double cnt = (double)size[best];
+    for (int i = 0; i < d; ++i) {
+        double mu = (double)cent[(long)best * d + i];
+        double nu = mu + (widen(k_new, i, dtype) - mu) / cnt;
+        cent[(long)best * d + i] = (float)nu;
+        ++ops;
+    }
+    if (madds)
+        *madds = ops;
+    return best;
+}

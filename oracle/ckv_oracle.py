@@ -1,0 +1,256 @@
+"""Python driver for the fp64 CPU oracle (ckv_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark may use it; the product path never imports it.  It shares no
+code with the HIP library and does not import it.
+
+The C file implements one graph's score, selection, index list, attention and
+local update in fp64.  This driver holds the host state of a whole decode layer
+(centroids, CSR member lists, the logical K/V cache, sequence lengths) and runs
+the per-graph functions for every graph of a decode step, the graphs spread over
+a thread pool (ctypes releases the GIL during each C call).
+
+Graph numbering follows the GQA layout: graph g = (b*Hkv + kvh)*gpk + j, where
+gpk = 1 (one graph per query group: heads kvh*G .. kvh*G+G-1 share it) or
+gpk = G (one graph per query head, j = head index inside the group)
+(rit.work post "CommunityKV long-context decoding", section on how many graphs a
+model keeps).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "ckv_oracle.c")
+LIB = os.path.join(HERE, "libckv_oracle.so")
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+DT_F32 = 0
+DT_BF16 = 1
+
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (fp64, no contraction of multiply-adds)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = os.environ.get("CKV_ORACLE_LIB")   # a planted-mistake build, in tests
+            if path is None:
+                path = LIB
+                if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+                    build()
+            L = C.CDLL(path)
+            P = C.c_void_p
+            i32 = C.c_int
+            L.ckvo_score.argtypes = [i32, i32, P, i32, P, P, i32, C.c_float, P]
+            L.ckvo_score.restype = None
+            L.ckvo_select.argtypes = [i32, P, P, i32, i32, P, P, C.POINTER(C.c_int)]
+            L.ckvo_select.restype = i32
+            L.ckvo_index_list.argtypes = [i32, i32, i32, P, P, P, P, P]
+            L.ckvo_index_list.restype = i32
+            L.ckvo_attend.argtypes = [i32, P, i32, P, P, i32, C.c_long, P, i32, C.c_float, P]
+            L.ckvo_attend.restype = None
+            L.ckvo_update.argtypes = [i32, P, i32, P, i32, P, P, P, P, P, i32,
+                                      C.POINTER(C.c_long)]
+            L.ckvo_update.restype = i32
+            _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def _dt(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return DT_BF16
+    if a.dtype == np.float32:
+        return DT_F32
+    raise TypeError(f"oracle inputs are bf16 bits (uint16) or float32, got {a.dtype}")
+
+
+# ---- single-graph wrappers (numpy in, numpy out) ---------------------------------
+
+def score(q: np.ndarray, cent: np.ndarray, size: np.ndarray, scale: float) -> np.ndarray:
+    """q [G, d] (uint16 bf16 bits or float32), cent [C, d] fp32, size [C] -> fp32 [C]."""
+    q = np.ascontiguousarray(q)
+    cent = np.ascontiguousarray(cent, np.float32)
+    size = np.ascontiguousarray(size, np.int32)
+    G, d = q.shape
+    Cn = cent.shape[0]
+    out = np.empty(Cn, np.float32)
+    lib().ckvo_score(d, G, _p(q), _dt(q), _p(cent), _p(size), Cn, scale, _p(out))
+    return out
+
+
+def select(score: np.ndarray, size: np.ndarray, budget: int, M: int):
+    """-> (sel u8 [C], k*, cand int32 [<=M])."""
+    score = np.ascontiguousarray(score, np.float32)
+    size = np.ascontiguousarray(size, np.int32)
+    Cn = score.shape[0]
+    sel = np.zeros(max(Cn, 1), np.uint8)
+    cand = np.full(max(M, 1), -1, np.int32)
+    nc = C.c_int(0)
+    k = lib().ckvo_select(Cn, _p(score), _p(size), int(budget), int(M), _p(sel), _p(cand),
+                          C.byref(nc))
+    return sel[:Cn], k, cand[:nc.value]
+
+
+def index_list(n: int, S: int, sel: np.ndarray, start: np.ndarray, size: np.ndarray,
+               members: np.ndarray, max_len: int) -> np.ndarray:
+    sel = np.ascontiguousarray(sel, np.uint8)
+    start = np.ascontiguousarray(start, np.int32)
+    size = np.ascontiguousarray(size, np.int32)
+    members = np.ascontiguousarray(members, np.int32)
+    idx = np.empty(max(max_len, 1), np.int32)
+    ln = lib().ckvo_index_list(int(n), int(S), sel.shape[0], _p(sel), _p(start), _p(size),
+                               _p(members), _p(idx))
+    assert ln <= max_len
+    return idx[:ln].copy()
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray, scale: float):
+    """q [d]; K, V [rows, d] (same dtype); idx [len] -> fp64 [d]."""
+    q = np.ascontiguousarray(q)
+    K = np.ascontiguousarray(K)
+    V = np.ascontiguousarray(V)
+    idx = np.ascontiguousarray(idx, np.int32)
+    d = q.shape[0]
+    out = np.empty(d, np.float64)
+    lib().ckvo_attend(d, _p(q), _dt(q), _p(K), _p(V), _dt(K), K.shape[1], _p(idx),
+                      idx.shape[0], scale, _p(out))
+    return out
+
+
+def update(k_new: np.ndarray, cand: np.ndarray, cent: np.ndarray, size: np.ndarray,
+           cap: np.ndarray, start: np.ndarray, members: np.ndarray, n: int):
+    """In-place update of cent/size/members.  -> (chosen id or <0, multiply-adds)."""
+    for a in (cent, size, members):
+        assert a.flags["C_CONTIGUOUS"] and a.flags["WRITEABLE"]
+    cand = np.ascontiguousarray(cand, np.int32)
+    cap = np.ascontiguousarray(cap, np.int32)
+    start = np.ascontiguousarray(start, np.int32)
+    k_new = np.ascontiguousarray(k_new)
+    ops = C.c_long(0)
+    r = lib().ckvo_update(cent.shape[1], _p(k_new), _dt(k_new), _p(cand), cand.shape[0],
+                          _p(cent), _p(size), _p(cap), _p(start), _p(members), int(n),
+                          C.byref(ops))
+    return r, ops.value
+
+
+# ---- a whole decode layer -----------------------------------------------------------
+
+ERR_CAPACITY = 1
+
+
+class OracleState:
+    """Host state of one decode layer, advanced one step at a time.
+
+    centroids [NG, Cmax, d] fp32; num_comms [NG]; comm_start/size/cap [NG, Cmax];
+    members [pool]; K, V [B, Hkv, n_alloc, d] raw (uint16 bf16 bits or float32),
+    logical token order; seq_len [B].
+    """
+
+    def __init__(self, *, B, Hq, Hkv, d, gpk, S, centroids, num_comms, comm_start,
+                 comm_size, comm_cap, members, K, V, seq_len, threads=None):
+        self.B, self.Hq, self.Hkv, self.d, self.gpk, self.S = B, Hq, Hkv, d, gpk, S
+        self.G = Hq // Hkv
+        self.NG = B * Hkv * gpk
+        self.cent = np.array(centroids, np.float32, copy=True, order="C")
+        self.num_comms = np.array(num_comms, np.int32, copy=True)
+        self.start = np.array(comm_start, np.int32, copy=True, order="C")
+        self.size = np.array(comm_size, np.int32, copy=True, order="C")
+        self.cap = np.array(comm_cap, np.int32, copy=True, order="C")
+        self.members = np.array(members, np.int32, copy=True, order="C")
+        self.K = np.array(K, copy=True, order="C")
+        self.V = np.array(V, copy=True, order="C")
+        self.seq_len = np.array(seq_len, np.int32, copy=True)
+        self.threads = threads or len(os.sched_getaffinity(0))
+
+    def heads_of(self, g: int):
+        j = g % self.gpk
+        kvh = (g // self.gpk) % self.Hkv
+        if self.gpk == 1:
+            return list(range(kvh * self.G, (kvh + 1) * self.G))
+        return [kvh * self.G + j]
+
+    def _graph_step(self, g, q, k_new, budget, scale, M, max_len, res):
+        b = g // (self.Hkv * self.gpk)
+        kvh = (g // self.gpk) % self.Hkv
+        n = int(self.seq_len[b])
+        Cn = int(self.num_comms[g])
+        heads = self.heads_of(g)
+        size = self.size[g, :Cn].copy()
+        s = score(q[b, heads], self.cent[g, :Cn], size, scale)
+        sel, k, cand = select(s, size, int(budget[b]), M)
+        idx = index_list(n, self.S, sel, self.start[g, :Cn], size, self.members, max_len)
+        K = self.K[b, kvh]
+        V = self.V[b, kvh]
+        outs = {h: attend(q[b, h], K, V, idx, scale) for h in heads}
+        # local update on this graph's own rows (views into the state arrays)
+        cent_g = self.cent[g, :Cn]
+        size_g = self.size[g, :Cn]
+        r, _ = update(k_new[b, kvh], cand, cent_g, size_g, self.cap[g, :Cn],
+                      self.start[g, :Cn], self.members, n) if Cn else (-2, 0)
+        res[g] = (s, sel, k, cand, idx, outs, r)
+
+    def step(self, q, k_new, v_new, budget, scale, M, max_len):
+        """One decode step for every graph.  q [B, Hq, d], k_new/v_new [B, Hkv, d] raw."""
+        q = np.ascontiguousarray(q)
+        k_new = np.ascontiguousarray(k_new)
+        res = [None] * self.NG
+        with ThreadPoolExecutor(self.threads) as ex:
+            list(ex.map(lambda g: self._graph_step(g, q, k_new, budget, scale, M, max_len,
+                                                   res), range(self.NG)))
+        Cmax = self.cent.shape[1]
+        out = {
+            "scores": np.full((self.NG, Cmax), -np.inf, np.float32),
+            "selected": np.zeros((self.NG, Cmax), np.uint8),
+            "kstar": np.zeros(self.NG, np.int32),
+            "cand": np.full((self.NG, M), -1, np.int32),
+            "idx": [None] * self.NG,
+            "idx_len": np.zeros(self.NG, np.int32),
+            "out": np.zeros((self.B, self.Hq, self.d), np.float64),
+            "assigned": np.full(self.NG, -1, np.int32),
+            "err": np.zeros(self.NG, np.int32),
+        }
+        for g, (s, sel, k, cand, idx, outs, r) in enumerate(res):
+            b = g // (self.Hkv * self.gpk)
+            Cn = len(s)
+            out["scores"][g, :Cn] = s
+            out["selected"][g, :Cn] = sel
+            out["kstar"][g] = k
+            out["cand"][g, :len(cand)] = cand
+            out["idx"][g] = idx
+            out["idx_len"][g] = len(idx)
+            for h, o in outs.items():
+                out["out"][b, h] = o
+            if r >= 0:
+                out["assigned"][g] = r
+            elif r == -1:
+                out["err"][g] |= ERR_CAPACITY
+        # append the new token's key/value at position n, then grow the sequence
+        for b in range(self.B):
+            n = int(self.seq_len[b])
+            self.K[b, :, n] = k_new[b]
+            self.V[b, :, n] = v_new[b]
+            self.seq_len[b] = n + 1
+        return out

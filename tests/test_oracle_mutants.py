@@ -1,0 +1,70 @@
+"""Planted mistakes: each mutant is a copy of the oracle's C source with one
+plausible slip (a dropped term, a wrong sign or index, a swapped operand, an
+off-by-one).  The pin suite must fail on every one of them; a mutant that passes
+would mean the pins leave that part of the oracle unchecked.  CPU only."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import ckv_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "score-drops-last-term": (
+        "for (int i = 0; i < d; ++i)\n                dot = dot + widen(q",
+        "for (int i = 0; i < d - 1; ++i)\n                dot = dot + widen(q"),
+    "score-no-scale": ("out[c] = (float)(best * (double)scale);", "out[c] = (float)best;"),
+    "score-last-head-not-max": ("if (dot > best)\n                best = dot;",
+                                "best = dot;"),
+    "score-transposed-centroid": ("q_dtype) * (double)cent[(long)c * d + i]",
+                                  "q_dtype) * (double)cent[(long)i * C + c]"),
+    "select-strict-budget": ("total + size[it[k].c] <= (long)budget",
+                             "total + size[it[k].c] < (long)budget"),
+    "select-tie-high-id-first": ("return (x->c < y->c) ? -1 : (x->c > y->c);",
+                                 "return (x->c > y->c) ? -1 : (x->c < y->c);"),
+    "select-ascending-score": ("if (x->s > y->s) return -1;\n    if (x->s < y->s) return 1;",
+                               "if (x->s < y->s) return -1;\n    if (x->s > y->s) return 1;"),
+    "select-skips-misfits": ("while (k < m && total + size[it[k].c] <= (long)budget) {\n"
+                             "        total += size[it[k].c];\n"
+                             "        sel[it[k].c] = 1;\n        ++k;\n    }",
+                             "for (int t = 0; t < m; ++t) {\n"
+                             "        if (total + size[it[t].c] > (long)budget) continue;\n"
+                             "        total += size[it[t].c];\n"
+                             "        sel[it[t].c] = 1;\n        ++k;\n    }"),
+    "list-drops-a-sink": ("for (int j = 0; j < ns; ++j)\n        idx[len++] = j;",
+                          "for (int j = 1; j < ns; ++j)\n        idx[len++] = j;"),
+    "list-drops-last-member": ("for (int j = 0; j < size[c]; ++j)\n            idx[len++]",
+                               "for (int j = 0; j < size[c] - 1; ++j)\n            idx[len++]"),
+    "attend-no-scale": ("z[t] = dot * (double)scale;", "z[t] = dot;"),
+    "attend-no-normalise": ("out[i] = out[i] / denom;", "out[i] = out[i];"),
+    "attend-values-from-keys": ("widen(V, row + i, kv_dtype)", "widen(K, row + i, kv_dtype)"),
+    "update-farthest": ("if (dist < best_d || (dist == best_d && c < best))",
+                        "if (best < 0 || dist > best_d || (dist == best_d && c < best))"),
+    "update-tie-high-id": ("(dist == best_d && c < best)", "(dist == best_d && c > best)"),
+    "update-wrong-count": ("double cnt = (double)size[best];",
+                           "double cnt = (double)size[best] + 1.0;"),
+    "update-wrong-position": ("members[start[best] + size[best]] = n;",
+                              "members[start[best] + size[best]] = n - 1;"),
+    "update-no-square": ("dist = dist + diff * diff;", "dist = dist + diff;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(O.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mut = tmp_path / "mut.c"
+    mut.write_text(src.replace(old, new))
+    so = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", *O.CFLAGS, str(mut), "-o", str(so), "-lm"])
+    env = dict(os.environ, CKV_ORACLE_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
