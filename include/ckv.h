@@ -1,0 +1,202 @@
+/*
+ * ckv.h -- C ABI of libckv.so, the CommunityKV decode hot path for MI355X (gfx950).
+ *
+ * Sources for the operations (the method is described in prose only):
+ *   [RIT-graph]  rit.work post "CommunityKV long-context decoding", section
+ *                "Граф токенов заменяет повторную кластеризацию" (the token graph
+ *                replaces repeated clustering): centres per community, the query
+ *                compared with the centres only, chosen communities loaded from
+ *                the full cache, exact attention inside them, sinks always added,
+ *                the cache never evicted, new tokens attached locally with one
+ *                centre updated.
+ *   [RIT-granul] same post, section "Ускорение зависит от того, сколько графов
+ *                хранит модель": one graph per group of heads sharing K/V, or one
+ *                per query head; a small active token budget.
+ *   [ABSTRACT]   "CommunityKV: Efficient Long-Context Decoding via Graph
+ *                Partitioning" (McKenna et al., 2026), abstract: constant-time
+ *                local update rule, per-head and query-group graphs.
+ *
+ * One decode step of one layer is, in stream order:
+ *   ckv_score_centroids -> ckv_select -> ckv_sparse_decode_attn -> ckv_local_update
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every array pointer is DEVICE memory owned by the caller; the library never
+ *   allocates or frees memory, keeps no pointer after a call returns and holds no
+ *   global state.  Structs (ckv_dims, ckv_graphs, ckv_kv) are read on the host
+ *   during the call only.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *   call only enqueues work on it and returns; there is no host synchronisation.
+ * - Host-detectable errors are returned synchronously and nothing is enqueued.
+ *   Data-dependent anomalies found on the device set bits in the caller's int32
+ *   `err_flag` (device memory, OR-ed, sticky) and the affected graph or token is
+ *   skipped; kernels never trap.  CKV_ERR_HIP reports a failed launch.
+ * - Graphs: NG = batch * num_kv_heads * graphs_per_kv.  Graph g of sequence b,
+ *   KV head kvh and sub-index j is g = (b*num_kv_heads + kvh)*graphs_per_kv + j.
+ *   With graphs_per_kv == 1 the G = num_q_heads/num_kv_heads query heads
+ *   kvh*G .. kvh*G+G-1 share one graph (query-group graph); with
+ *   graphs_per_kv == G query head kvh*G + j owns graph g (per-head graph).
+ * - Not reentrant across overlapping calls that share a workspace.
+ */
+#ifndef CKV_H
+#define CKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CKV_API __attribute__((visibility("default")))
+
+typedef int32_t ckv_status;
+enum {
+    CKV_OK = 0,
+    CKV_ERR_INVALID_ARG = -1, /* null pointer, inconsistent sizes            */
+    CKV_ERR_UNSUPPORTED = -2, /* head_dim / dtype / group size not built      */
+    CKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required   */
+    CKV_ERR_HIP = -4          /* a kernel launch failed                       */
+};
+
+enum { CKV_DT_F32 = 0, CKV_DT_BF16 = 1 };
+
+/* Sticky device error bits OR-ed into *err_flag. */
+enum {
+    CKV_DEVERR_CAPACITY = 1,      /* chosen community has no free member slot   */
+    CKV_DEVERR_UNMAPPED_PAGE = 2, /* page_table entry < 0 or >= num_pages        */
+    CKV_DEVERR_INDEX_RANGE = 4    /* index list entry outside [0, seq_len)       */
+};
+
+/* Largest supported values. */
+enum { CKV_MAX_COMMS = 4096, CKV_MAX_CAND = 16 };
+
+typedef struct ckv_dims {
+    int32_t batch;         /* B sequences                                          */
+    int32_t num_q_heads;   /* Hq                                                   */
+    int32_t num_kv_heads;  /* Hkv; Hq % Hkv == 0, G = Hq/Hkv in {1,2,4,8}           */
+    int32_t head_dim;      /* d in {64, 128}                                       */
+    int32_t graphs_per_kv; /* 1 (query-group graph) or G (one graph per query head) */
+    int32_t max_comms;     /* Cmax: stride of per-community arrays; multiple of 64, */
+                           /* <= CKV_MAX_COMMS                                      */
+    int32_t num_sinks;     /* S >= 0: positions 0..S-1 are attention sinks          */
+    int32_t dtype;         /* CKV_DT_BF16 or CKV_DT_F32: q, K, V, k_new, v_new      */
+} ckv_dims;
+
+/* Community state of NG graphs.  Community c of graph g owns member slots
+ * members[comm_start[g*Cmax+c] .. + comm_cap[g*Cmax+c]); the first
+ * comm_size[g*Cmax+c] hold token positions in ascending order of insertion. */
+typedef struct ckv_graphs {
+    float *centroids;    /* fp32, "community-interleaved": element i of centroid c of
+                            graph g at centroids[((g*(d/4) + i/4)*Cmax + c)*4 + i%4] */
+    int32_t *num_comms;  /* [NG] communities in use, C_g <= Cmax                     */
+    int32_t *comm_start; /* [NG*Cmax]                                                 */
+    int32_t *comm_size;  /* [NG*Cmax]                                                 */
+    int32_t *comm_cap;   /* [NG*Cmax]                                                 */
+    int32_t *members;    /* member pool (token positions)                            */
+} ckv_graphs;
+
+/* Full, never-evicted paged KV cache of one layer. */
+typedef struct ckv_kv {
+    void *k;                  /* [num_pages][Hkv][page_size][d] in dims.dtype        */
+    void *v;                  /* same layout                                         */
+    const int32_t *page_table; /* [B][max_pages_per_seq]: physical page of logical
+                                  page p of sequence b; < 0 = unmapped               */
+    int32_t page_size;         /* tokens per page, power of two                      */
+    int32_t max_pages_per_seq;
+    int32_t num_pages;
+    int32_t *seq_len;          /* [B] tokens in cache; ckv_local_update adds one     */
+} ckv_kv;
+
+/* Bytes of workspace ckv_sparse_decode_attn needs for index lists of up to
+ * `index_stride` entries per graph.  Returns 0 for invalid dims. */
+CKV_API size_t ckv_workspace_size(const ckv_dims *dims, int32_t index_stride);
+
+/* Zero the workspace's arrival counters (a fill kernel, no memset node).  Call
+ * once after allocating it; the kernels leave it zeroed after every call. */
+CKV_API ckv_status ckv_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Layout helpers: rows [NG][Cmax][d] fp32 <-> community-interleaved centroids. */
+CKV_API ckv_status ckv_centroids_from_rows(const ckv_dims *dims, const float *rows,
+                                   float *centroids, void *stream);
+CKV_API ckv_status ckv_centroids_to_rows(const ckv_dims *dims, const float *centroids,
+                                 float *rows, void *stream);
+
+/*
+ * Centroid scoring [RIT-graph: the decode query is compared with the community
+ * centres only; RIT-granul: a group graph serves all heads of the group].
+ *   scores[g*Cmax + c] = fp32( max_{h in heads(g)} (q_h . mu_{g,c}) * scale )
+ * with the inner products accumulated in fp64 in element order (the products of
+ * bf16/fp32 inputs and fp32 centroids are exact in fp64); -inf if the community
+ * is empty.  Entries c >= num_comms[g] are not written.
+ *   q      : [B][Hq][d] in dims.dtype
+ *   scale  : usually 1/sqrt(d)
+ *   q_ws   : device scratch of ckv_score_workspace_size(dims) bytes (fp64 copy of q)
+ */
+CKV_API size_t ckv_score_workspace_size(const ckv_dims *dims);
+CKV_API ckv_status ckv_score_centroids(const ckv_dims *dims, const void *q, const ckv_graphs *graphs,
+                               float scale, float *scores, void *q_ws, size_t q_ws_bytes,
+                               void *stream);
+
+/*
+ * Budgeted community selection, sinks and compaction [RIT-granul: small active
+ * token budget; RIT-graph: whole communities are loaded, sinks always added].
+ * Per graph: order the non-empty communities by (score desc, id asc) and keep
+ * the longest prefix whose sizes sum to <= budget[b] (sinks not counted; stop at
+ * the first community that does not fit).  Then
+ *   index_list[g*index_stride ..] = 0..min(S,n)-1, then the members of the kept
+ *   communities in ascending id, each in member order;   n = kv_seq_len[b]
+ *   index_len[g] = its length;  num_selected[g] = number kept (may be NULL)
+ *   cand[g*n_cand + i] = i-th community of the same order (i < n_cand), -1 if none
+ *   selected[g*Cmax + c] = 1 if kept else 0 (may be NULL)
+ * Returns CKV_ERR_INVALID_ARG if index_stride < S + max budget is not
+ * guaranteed by the caller; budgets are read on the device, so the caller must
+ * ensure S + budget[b] <= index_stride (entries beyond are dropped and flagged
+ * CKV_DEVERR_INDEX_RANGE).
+ */
+CKV_API ckv_status ckv_select(const ckv_dims *dims, const float *scores, const ckv_graphs *graphs,
+                      const int32_t *budget, const int32_t *kv_seq_len, int32_t n_cand,
+                      int32_t *index_list, int32_t index_stride, int32_t *index_len,
+                      int32_t *num_selected, int32_t *cand, uint8_t *selected,
+                      int32_t *err_flag, void *stream);
+
+/*
+ * Sparse exact attention over the index lists [RIT-graph: exact attention inside
+ * the reduced token set; the cache stays full, so any token can be chosen].
+ * For every query head h of sequence b, with graph g(h):
+ *   out[(b*Hq + h)*d + i] = sum_j softmax_j(scale * q_h . K_j) V_j[i]
+ * over j in index_list[g*index_stride .. + index_len[g]), K/V rows read through
+ * the page table.  fp32 accumulation, fp32 output; an empty list gives 0.
+ * Entries outside [0, seq_len[b]) or on unmapped pages are skipped and flagged.
+ * ws: ckv_workspace_size(dims, index_stride) bytes, zeroed once by
+ * ckv_workspace_init.
+ */
+CKV_API ckv_status ckv_sparse_decode_attn(const ckv_dims *dims, const void *q, const ckv_kv *kv,
+                                  const int32_t *index_list, int32_t index_stride,
+                                  const int32_t *index_len, float scale, float *out,
+                                  void *ws, size_t ws_bytes, int32_t *err_flag, void *stream);
+
+/*
+ * Constant-time local update [RIT-graph: the new token joins a neighbouring
+ * community and one centre moves, at a cost set by d and not by the context;
+ * ABSTRACT: constant-time local update rule].  For every graph g of sequence b,
+ * with n = kv->seq_len[b] before the call:
+ *   c* = argmin over the candidates cand[g*n_cand ..] (entries < 0 ignored) of
+ *        ||k_new - mu_c||^2 (fp64, element order, lower id on ties)
+ *   members[start + size] = n; size += 1;
+ *   mu_c* = fp32( mu + (k_new - mu) / size )   (fp64 arithmetic per element)
+ *   assigned[g] = c* (-1 if no candidate or the community is full -> CAPACITY bit)
+ * and, once per (b, KV head), K/V row n <- k_new/v_new; finally seq_len[b] += 1.
+ *   k_new, v_new: [B][Hkv][d] in dims.dtype
+ */
+CKV_API ckv_status ckv_local_update(const ckv_dims *dims, const void *k_new, const void *v_new,
+                            const int32_t *cand, int32_t n_cand, const ckv_graphs *graphs,
+                            const ckv_kv *kv, int32_t *assigned, int32_t *err_flag,
+                            void *stream);
+
+CKV_API const char *ckv_status_string(ckv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CKV_H */

@@ -1,0 +1,274 @@
+"""ctypes binding of libckv.so: argument marshalling only.
+
+Each function has the name of the C entry point it calls and takes torch tensors
+that already live on the GPU; it passes their raw device pointers and the current
+HIP stream.  No computation happens here, and there is no fallback: if the HIP
+library is missing or fails, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libckv.so")
+
+CKV_OK = 0
+CKV_DT_F32 = 0
+CKV_DT_BF16 = 1
+DEVERR_CAPACITY = 1
+DEVERR_UNMAPPED_PAGE = 2
+DEVERR_INDEX_RANGE = 4
+
+
+class ckv_dims(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("graphs_per_kv", C.c_int32), ("max_comms", C.c_int32),
+                ("num_sinks", C.c_int32), ("dtype", C.c_int32)]
+
+
+class ckv_graphs(C.Structure):
+    _fields_ = [("centroids", C.c_void_p), ("num_comms", C.c_void_p), ("comm_start", C.c_void_p),
+                ("comm_size", C.c_void_p), ("comm_cap", C.c_void_p), ("members", C.c_void_p)]
+
+
+class ckv_kv(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("page_table", C.c_void_p),
+                ("page_size", C.c_int32), ("max_pages_per_seq", C.c_int32),
+                ("num_pages", C.c_int32), ("seq_len", C.c_void_p)]
+
+
+class CkvError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libckv.so (built by sparse_long_context_centroid_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise CkvError(f"{path} is missing: build it with "
+                       "`python -m sparse_long_context_centroid_amd.build`")
+    L = C.CDLL(path)
+    P, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+    pd, pg, pk = C.POINTER(ckv_dims), C.POINTER(ckv_graphs), C.POINTER(ckv_kv)
+    sig = {
+        "ckv_workspace_size": (sz, [pd, i32]),
+        "ckv_workspace_init": (i32, [P, sz, P]),
+        "ckv_centroids_from_rows": (i32, [pd, P, P, P]),
+        "ckv_centroids_to_rows": (i32, [pd, P, P, P]),
+        "ckv_score_workspace_size": (sz, [pd]),
+        "ckv_score_centroids": (i32, [pd, P, pg, C.c_float, P, P, sz, P]),
+        "ckv_select": (i32, [pd, P, pg, P, P, i32, P, i32, P, P, P, P, P, P]),
+        "ckv_sparse_decode_attn": (i32, [pd, P, pk, P, i32, P, C.c_float, P, P, sz, P, P]),
+        "ckv_local_update": (i32, [pd, P, P, P, i32, pg, pk, P, P, P]),
+        "ckv_status_string": (C.c_char_p, [i32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+EXPORTED = ("ckv_workspace_size", "ckv_workspace_init", "ckv_centroids_from_rows",
+            "ckv_centroids_to_rows", "ckv_score_workspace_size", "ckv_score_centroids",
+            "ckv_select", "ckv_sparse_decode_attn", "ckv_local_update", "ckv_status_string")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise CkvError("libckv takes device tensors")
+    if not t.is_contiguous():
+        raise CkvError("libckv takes contiguous tensors")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != CKV_OK:
+        msg = load().ckv_status_string(status).decode()
+        raise CkvError(f"{what} failed: {msg} ({status})")
+
+
+def make_dims(B, Hq, Hkv, d, gpk, Cmax, S, dtype) -> ckv_dims:
+    return ckv_dims(B, Hq, Hkv, d, gpk, Cmax, S, dtype)
+
+
+def make_graphs(centroids, num_comms, comm_start, comm_size, comm_cap, members) -> ckv_graphs:
+    return ckv_graphs(_ptr(centroids), _ptr(num_comms), _ptr(comm_start), _ptr(comm_size),
+                      _ptr(comm_cap), _ptr(members))
+
+
+def make_kv(k, v, page_table, page_size, seq_len) -> ckv_kv:
+    return ckv_kv(_ptr(k), _ptr(v), _ptr(page_table), page_size, page_table.shape[1],
+                  k.shape[0], _ptr(seq_len))
+
+
+# ---- entry points ---------------------------------------------------------------------
+
+def ckv_workspace_size(dims: ckv_dims, index_stride: int) -> int:
+    return load().ckv_workspace_size(C.byref(dims), index_stride)
+
+
+def ckv_workspace_init(ws: torch.Tensor, stream=None):
+    _check(load().ckv_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "ckv_workspace_init")
+
+
+def ckv_centroids_from_rows(dims, rows, centroids, stream=None):
+    _check(load().ckv_centroids_from_rows(C.byref(dims), _ptr(rows), _ptr(centroids),
+                                          _stream(stream)), "ckv_centroids_from_rows")
+
+
+def ckv_centroids_to_rows(dims, centroids, rows, stream=None):
+    _check(load().ckv_centroids_to_rows(C.byref(dims), _ptr(centroids), _ptr(rows),
+                                        _stream(stream)), "ckv_centroids_to_rows")
+
+
+def ckv_score_workspace_size(dims: ckv_dims) -> int:
+    return load().ckv_score_workspace_size(C.byref(dims))
+
+
+def ckv_score_centroids(dims, q, graphs, scale, scores, q_ws, stream=None):
+    _check(load().ckv_score_centroids(C.byref(dims), _ptr(q), C.byref(graphs), scale,
+                                      _ptr(scores), _ptr(q_ws), q_ws.numel() * q_ws.element_size(),
+                                      _stream(stream)), "ckv_score_centroids")
+
+
+def ckv_select(dims, scores, graphs, budget, seq_len, n_cand, index_list, index_len,
+               num_selected, cand, selected, err_flag, stream=None):
+    _check(load().ckv_select(C.byref(dims), _ptr(scores), C.byref(graphs), _ptr(budget),
+                             _ptr(seq_len), n_cand, _ptr(index_list), index_list.shape[1],
+                             _ptr(index_len), _ptr(num_selected), _ptr(cand), _ptr(selected),
+                             _ptr(err_flag), _stream(stream)), "ckv_select")
+
+
+def ckv_sparse_decode_attn(dims, q, kv, index_list, index_len, scale, out, ws, err_flag,
+                           stream=None):
+    _check(load().ckv_sparse_decode_attn(C.byref(dims), _ptr(q), C.byref(kv), _ptr(index_list),
+                                         index_list.shape[1], _ptr(index_len), scale, _ptr(out),
+                                         _ptr(ws), ws.numel() * ws.element_size(), _ptr(err_flag),
+                                         _stream(stream)), "ckv_sparse_decode_attn")
+
+
+def ckv_local_update(dims, k_new, v_new, cand, n_cand, graphs, kv, assigned, err_flag,
+                     stream=None):
+    _check(load().ckv_local_update(C.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(cand), n_cand,
+                                   C.byref(graphs), C.byref(kv), _ptr(assigned), _ptr(err_flag),
+                                   _stream(stream)), "ckv_local_update")
+
+
+def ckv_status_string(status: int) -> str:
+    return load().ckv_status_string(status).decode()
+
+
+# ---- device state of one decode layer ----------------------------------------------------
+
+class DecodeLayer:
+    """Device buffers of one layer (graphs, paged KV, outputs, workspaces) and the
+    four calls of one decode step.  Built from host/device arrays; every step of
+    the path runs in libckv's kernels."""
+
+    def __init__(self, *, B, Hq, Hkv, d, gpk, S, dtype, Cmax, M, index_stride, page_size,
+                 centroid_rows, num_comms, comm_start, comm_size, comm_cap, members,
+                 k_pages, v_pages, page_table, seq_len, budget, device="cuda"):
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.dims = make_dims(B, Hq, Hkv, d, gpk, Cmax, S, dtype)
+        self.B, self.Hq, self.Hkv, self.d, self.gpk, self.S, self.M = B, Hq, Hkv, d, gpk, S, M
+        self.Cmax = Cmax
+        self.NG = B * Hkv * gpk
+        self.page_size = page_size
+        t = lambda a: torch.as_tensor(a).to(**i32).contiguous()
+        self.num_comms = t(num_comms)
+        self.comm_start = t(comm_start)
+        self.comm_size = t(comm_size)
+        self.comm_cap = t(comm_cap)
+        self.members = t(members)
+        self.centroids = torch.empty(self.NG * Cmax * d, dtype=torch.float32, device=dev)
+        rows = centroid_rows.to(dev, torch.float32).contiguous()
+        ckv_centroids_from_rows(self.dims, rows, self.centroids)
+        self.k = k_pages.to(dev).contiguous()
+        self.v = v_pages.to(dev).contiguous()
+        self.page_table = t(page_table)
+        self.seq_len = t(seq_len)
+        self.budget = t(budget)
+        self.graphs = make_graphs(self.centroids, self.num_comms, self.comm_start,
+                                  self.comm_size, self.comm_cap, self.members)
+        self.kv = make_kv(self.k, self.v, self.page_table, page_size, self.seq_len)
+        # outputs and workspaces
+        self.scores = torch.full((self.NG, Cmax), float("-inf"), dtype=torch.float32, device=dev)
+        self.q_ws = torch.empty(ckv_score_workspace_size(self.dims), dtype=torch.uint8,
+                                device=dev)
+        self.index_list = torch.zeros((self.NG, index_stride), **i32)
+        self.index_len = torch.zeros(self.NG, **i32)
+        self.num_selected = torch.zeros(self.NG, **i32)
+        self.cand = torch.zeros((self.NG, M), **i32)
+        self.selected = torch.zeros((self.NG, Cmax), dtype=torch.uint8, device=dev)
+        self.assigned = torch.zeros(self.NG, **i32)
+        self.err = torch.zeros(1, **i32)
+        self.out = torch.zeros((B, Hq, d), dtype=torch.float32, device=dev)
+        wsz = ckv_workspace_size(self.dims, index_stride)
+        if wsz == 0:
+            raise CkvError("invalid dims for the workspace")
+        self.ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+        ckv_workspace_init(self.ws)
+
+    # individual stages
+    def score(self, q, scale):
+        ckv_score_centroids(self.dims, q, self.graphs, scale, self.scores, self.q_ws)
+
+    def select(self):
+        ckv_select(self.dims, self.scores, self.graphs, self.budget, self.seq_len, self.M,
+                   self.index_list, self.index_len, self.num_selected, self.cand,
+                   self.selected, self.err)
+
+    def attend(self, q, scale):
+        ckv_sparse_decode_attn(self.dims, q, self.kv, self.index_list, self.index_len, scale,
+                               self.out, self.ws, self.err)
+
+    def update(self, k_new, v_new):
+        ckv_local_update(self.dims, k_new, v_new, self.cand, self.M, self.graphs, self.kv,
+                         self.assigned, self.err)
+
+    def step(self, q, k_new, v_new, scale):
+        self.score(q, scale)
+        self.select()
+        self.attend(q, scale)
+        self.update(k_new, v_new)
+
+    def centroid_rows(self) -> torch.Tensor:
+        rows = torch.empty((self.NG, self.Cmax, self.d), dtype=torch.float32,
+                           device=self.centroids.device)
+        ckv_centroids_to_rows(self.dims, self.centroids, rows)
+        return rows
+
+
+def decode_layer_from_workload(wl, li: int = 0, index_stride: Optional[int] = None,
+                               device: str = "cuda") -> DecodeLayer:
+    """Device state of layer `li` of a generated workload (inputs.make_workload)."""
+    L = wl.layers[li]
+    if index_stride is None:
+        index_stride = int(wl.S + wl.budget.max())
+    return DecodeLayer(B=wl.B, Hq=wl.Hq, Hkv=wl.Hkv, d=wl.d, gpk=wl.gpk, S=wl.S,
+                       dtype=wl.dtype, Cmax=wl.Cmax, M=wl.M, index_stride=index_stride,
+                       page_size=wl.page_size, centroid_rows=L.centroids,
+                       num_comms=L.num_comms, comm_start=L.comm_start, comm_size=L.comm_size,
+                       comm_cap=L.comm_cap, members=L.members, k_pages=L.k_pages,
+                       v_pages=L.v_pages, page_table=wl.page_table, seq_len=wl.seq_len0,
+                       budget=wl.budget, device=device)

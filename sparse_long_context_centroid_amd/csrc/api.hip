@@ -1,0 +1,172 @@
+// api.hip -- the extern "C" entry points of libckv.so: host-side validation, then
+// launches on the caller's stream.  No allocation, no synchronisation, no state.
+#include <hip/hip_runtime.h>
+
+#include "ckv.h"
+#include "ckv_internal.h"
+
+using ckv::Problem;
+
+namespace {
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+ckv_status make_problem(const ckv_dims *d, Problem &p) {
+    if (!d) return CKV_ERR_INVALID_ARG;
+    if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->num_sinks < 0 ||
+        d->max_comms < 64 || d->max_comms % 64 != 0)
+        return CKV_ERR_INVALID_ARG;
+    if (d->num_q_heads % d->num_kv_heads != 0) return CKV_ERR_INVALID_ARG;
+    const int G = d->num_q_heads / d->num_kv_heads;
+    if (d->graphs_per_kv != 1 && d->graphs_per_kv != G) return CKV_ERR_INVALID_ARG;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return CKV_ERR_UNSUPPORTED;
+    if (d->head_dim != 64 && d->head_dim != 128) return CKV_ERR_UNSUPPORTED;
+    if (d->dtype != CKV_DT_BF16 && d->dtype != CKV_DT_F32) return CKV_ERR_UNSUPPORTED;
+    if (d->max_comms > CKV_MAX_COMMS) return CKV_ERR_UNSUPPORTED;
+    p.B = d->batch;
+    p.Hq = d->num_q_heads;
+    p.Hkv = d->num_kv_heads;
+    p.D = d->head_dim;
+    p.gpk = d->graphs_per_kv;
+    p.Cmax = d->max_comms;
+    p.S = d->num_sinks;
+    p.dtype = d->dtype;
+    if ((long long)p.NG() * p.Cmax * p.D > (1LL << 40)) return CKV_ERR_INVALID_ARG;
+    return CKV_OK;
+}
+
+ckv_status check_graphs(const ckv_graphs *g) {
+    if (!g || !g->centroids || !g->num_comms || !g->comm_start || !g->comm_size ||
+        !g->comm_cap || !g->members)
+        return CKV_ERR_INVALID_ARG;
+    return CKV_OK;
+}
+
+ckv_status check_kv(const ckv_kv *kv) {
+    if (!kv || !kv->k || !kv->v || !kv->page_table || !kv->seq_len) return CKV_ERR_INVALID_ARG;
+    if (!is_pow2(kv->page_size) || kv->page_size > 4096 || kv->max_pages_per_seq < 1 ||
+        kv->num_pages < 1)
+        return CKV_ERR_INVALID_ARG;
+    return CKV_OK;
+}
+
+ckv_status hip_status(hipError_t e) { return e == hipSuccess ? CKV_OK : CKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t ckv_workspace_size(const ckv_dims *dims, int32_t index_stride) {
+    Problem p;
+    if (make_problem(dims, p) != CKV_OK || index_stride < 1) return 0;
+    return ckv::attn_counter_bytes(p) + ckv::attn_partial_floats(p, index_stride) * sizeof(float);
+}
+
+ckv_status ckv_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+    if (!ws || ws_bytes == 0) return CKV_ERR_INVALID_ARG;
+    return hip_status(ckv::launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)));
+}
+
+ckv_status ckv_centroids_from_rows(const ckv_dims *dims, const float *rows, float *centroids,
+                                   void *stream) {
+    Problem p;
+    ckv_status s = make_problem(dims, p);
+    if (s != CKV_OK) return s;
+    if (!rows || !centroids || rows == centroids) return CKV_ERR_INVALID_ARG;
+    return hip_status(ckv::launch_rows_to_interleaved(p, rows, centroids,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
+ckv_status ckv_centroids_to_rows(const ckv_dims *dims, const float *centroids, float *rows,
+                                 void *stream) {
+    Problem p;
+    ckv_status s = make_problem(dims, p);
+    if (s != CKV_OK) return s;
+    if (!rows || !centroids || rows == centroids) return CKV_ERR_INVALID_ARG;
+    return hip_status(ckv::launch_interleaved_to_rows(p, centroids, rows,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t ckv_score_workspace_size(const ckv_dims *dims) {
+    Problem p;
+    if (make_problem(dims, p) != CKV_OK) return 0;
+    return (size_t)p.NG() * p.heads_per_graph() * p.D * sizeof(double);
+}
+
+ckv_status ckv_score_centroids(const ckv_dims *dims, const void *q, const ckv_graphs *graphs,
+                               float scale, float *scores, void *q_ws, size_t q_ws_bytes,
+                               void *stream) {
+    Problem p;
+    ckv_status s = make_problem(dims, p);
+    if (s != CKV_OK) return s;
+    if ((s = check_graphs(graphs)) != CKV_OK) return s;
+    if (!q || !scores) return CKV_ERR_INVALID_ARG;
+    if (!q_ws || q_ws_bytes < ckv_score_workspace_size(dims)) return CKV_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    double *q64 = static_cast<double *>(q_ws);
+    if ((s = hip_status(ckv::launch_stage_query(p, q, q64, st))) != CKV_OK) return s;
+    return hip_status(ckv::launch_score(p, q64, *graphs, (double)scale, scores, st));
+}
+
+ckv_status ckv_select(const ckv_dims *dims, const float *scores, const ckv_graphs *graphs,
+                      const int32_t *budget, const int32_t *kv_seq_len, int32_t n_cand,
+                      int32_t *index_list, int32_t index_stride, int32_t *index_len,
+                      int32_t *num_selected, int32_t *cand, uint8_t *selected,
+                      int32_t *err_flag, void *stream) {
+    Problem p;
+    ckv_status s = make_problem(dims, p);
+    if (s != CKV_OK) return s;
+    if ((s = check_graphs(graphs)) != CKV_OK) return s;
+    if (!scores || !budget || !kv_seq_len || !index_list || !index_len || !cand)
+        return CKV_ERR_INVALID_ARG;
+    if (n_cand < 1 || n_cand > CKV_MAX_CAND || index_stride < 1) return CKV_ERR_INVALID_ARG;
+    return hip_status(ckv::launch_select(p, scores, *graphs, budget, kv_seq_len, n_cand,
+                                         index_list, index_stride, index_len, num_selected, cand,
+                                         selected, err_flag, static_cast<hipStream_t>(stream)));
+}
+
+ckv_status ckv_sparse_decode_attn(const ckv_dims *dims, const void *q, const ckv_kv *kv,
+                                  const int32_t *index_list, int32_t index_stride,
+                                  const int32_t *index_len, float scale, float *out, void *ws,
+                                  size_t ws_bytes, int32_t *err_flag, void *stream) {
+    Problem p;
+    ckv_status s = make_problem(dims, p);
+    if (s != CKV_OK) return s;
+    if ((s = check_kv(kv)) != CKV_OK) return s;
+    if (!q || !index_list || !index_len || !out || index_stride < 1) return CKV_ERR_INVALID_ARG;
+    const size_t need = ckv_workspace_size(dims, index_stride);
+    if (!ws || ws_bytes < need) return CKV_ERR_WORKSPACE;
+    uint32_t *counters = static_cast<uint32_t *>(ws);
+    float *partials = reinterpret_cast<float *>(static_cast<char *>(ws) + ckv::attn_counter_bytes(p));
+    return hip_status(ckv::launch_attn(p, q, *kv, index_list, index_stride, index_len, scale, out,
+                                       counters, partials, err_flag,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+ckv_status ckv_local_update(const ckv_dims *dims, const void *k_new, const void *v_new,
+                            const int32_t *cand, int32_t n_cand, const ckv_graphs *graphs,
+                            const ckv_kv *kv, int32_t *assigned, int32_t *err_flag,
+                            void *stream) {
+    Problem p;
+    ckv_status s = make_problem(dims, p);
+    if (s != CKV_OK) return s;
+    if ((s = check_graphs(graphs)) != CKV_OK) return s;
+    if ((s = check_kv(kv)) != CKV_OK) return s;
+    if (!k_new || !v_new || !cand || !assigned) return CKV_ERR_INVALID_ARG;
+    if (n_cand < 1 || n_cand > CKV_MAX_CAND) return CKV_ERR_INVALID_ARG;
+    return hip_status(ckv::launch_update(p, k_new, v_new, cand, n_cand, *graphs, *kv, assigned,
+                                         err_flag, static_cast<hipStream_t>(stream)));
+}
+
+const char *ckv_status_string(ckv_status status) {
+    switch (status) {
+        case CKV_OK: return "ok";
+        case CKV_ERR_INVALID_ARG: return "invalid argument";
+        case CKV_ERR_UNSUPPORTED: return "unsupported configuration";
+        case CKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case CKV_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// ckv_device.h -- device helpers shared by the libckv kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ckv.h"
+
+namespace ckv {
+
+constexpr int kWave = 64;
+
+// ---- element types ---------------------------------------------------------------
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits_rne(float f) {
+    uint32_t b = __float_as_uint(f);
+    b = b + 0x7fffu + ((b >> 16) & 1u);
+    return static_cast<uint16_t>(b >> 16);
+}
+
+// ---- DPP lane exchanges inside a row of 16 lanes ------------------------------------
+// quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
+// row_mirror = 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// All-reduce sum over aligned groups of L lanes (L in {1,2,4,8,16,32,64}).
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (L >= 2) x += dpp<0xB1>(x);
+    if constexpr (L >= 4) x += dpp<0x4E>(x);
+    if constexpr (L >= 8) x += dpp<0x141>(x);
+    if constexpr (L >= 16) x += dpp<0x140>(x);
+    if constexpr (L >= 32) x += __shfl_xor(x, 16);
+    if constexpr (L >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Order-preserving map of an fp32 score to u32 (larger score -> larger key).
+__device__ __forceinline__ uint32_t order_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ void set_err(int32_t *err, int32_t bit) {
+    if (err) atomicOr(err, bit);
+}
+
+}  // namespace ckv

@@ -1,0 +1,135 @@
+"""GPU-vs-oracle comparison used by the GPU tests, the smoke check and the bench.
+
+The HIP path runs through the C ABI (binding.DecodeLayer); the oracle runs on host
+copies of exactly the same input bytes.  Acceptance:
+  * scores, selected sets, candidate lists, index lists, index lengths, assigned
+    communities, member lists and centroids: bit-exact (both sides compute the
+    inner products and the centroid update in fp64 from the same fp32/bf16 bytes
+    and round once to fp32);
+  * attention outputs: max-abs <= 2e-3 and relative L2 <= 1e-3 per (sequence,
+    head) against the fp64 oracle.
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import helpers as H
+from sparse_long_context_centroid_amd import binding as Bd
+
+ATOL = 2e-3
+RTOL_L2 = 1e-3
+
+
+class ParityError(AssertionError):
+    pass
+
+
+def _fail(msg):
+    raise ParityError(msg)
+
+
+def compare_step(layer: Bd.DecodeLayer, res: dict, wl, t: int, out_stats: list):
+    """Compare one step's device outputs with the oracle's result dict."""
+    NG = layer.NG
+    scores = layer.scores.cpu().numpy()
+    sel = layer.selected.cpu().numpy()
+    nsel = layer.num_selected.cpu().numpy()
+    cand = layer.cand.cpu().numpy()
+    ilen = layer.index_len.cpu().numpy()
+    idx = layer.index_list.cpu().numpy()
+    assigned = layer.assigned.cpu().numpy()
+    out = layer.out.cpu().numpy().astype(np.float64)
+    num_comms = layer.num_comms.cpu().numpy()
+    for g in range(NG):
+        C = int(num_comms[g])
+        a, b = scores[g, :C], res["scores"][g, :C]
+        if not np.array_equal(a.view(np.uint32), b.view(np.uint32)):
+            bad = np.nonzero(a.view(np.uint32) != b.view(np.uint32))[0]
+            _fail(f"step {t} graph {g}: {len(bad)} scores differ, first c={bad[0]} "
+                  f"gpu={a[bad[0]]!r} oracle={b[bad[0]]!r}")
+        if not np.array_equal(sel[g, :C], res["selected"][g, :C]) or sel[g, C:].any():
+            d = np.nonzero(sel[g, :C] != res["selected"][g, :C])[0]
+            _fail(f"step {t} graph {g}: selected sets differ at communities {d[:10]}")
+        if nsel[g] != res["kstar"][g]:
+            _fail(f"step {t} graph {g}: k* gpu={nsel[g]} oracle={res['kstar'][g]}")
+        if not np.array_equal(cand[g], res["cand"][g]):
+            _fail(f"step {t} graph {g}: candidates gpu={cand[g]} oracle={res['cand'][g]}")
+        if ilen[g] != res["idx_len"][g]:
+            _fail(f"step {t} graph {g}: index_len gpu={ilen[g]} oracle={res['idx_len'][g]}")
+        if not np.array_equal(idx[g, :ilen[g]], res["idx"][g]):
+            _fail(f"step {t} graph {g}: index lists differ")
+        if assigned[g] != res["assigned"][g]:
+            _fail(f"step {t} graph {g}: assigned gpu={assigned[g]} oracle={res['assigned'][g]}")
+    ref = res["out"]
+    err = np.abs(out - ref)
+    mx = float(err.max()) if err.size else 0.0
+    rel = np.linalg.norm(out - ref, axis=-1) / np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
+    out_stats.append((mx, float(rel.max()) if rel.size else 0.0))
+    if mx > ATOL:
+        bi, hi, di = np.unravel_index(int(err.argmax()), err.shape)
+        _fail(f"step {t}: attention max-abs {mx:.3e} > {ATOL} at (b={bi}, h={hi}, i={di})")
+    if rel.max() > RTOL_L2:
+        _fail(f"step {t}: attention relative L2 {rel.max():.3e} > {RTOL_L2}")
+
+
+def compare_state(layer: Bd.DecodeLayer, st, wl):
+    """Centroids, sizes, members and sequence lengths after the steps."""
+    rows = layer.centroid_rows().cpu().numpy()
+    size = layer.comm_size.cpu().numpy().reshape(st.size.shape)
+    members = layer.members.cpu().numpy()
+    seq = layer.seq_len.cpu().numpy()
+    if not np.array_equal(size, st.size):
+        _fail("community sizes differ")
+    if not np.array_equal(members, st.members):
+        _fail("member pools differ")
+    if not np.array_equal(seq, st.seq_len):
+        _fail(f"seq_len gpu={seq} oracle={st.seq_len}")
+    Kg, Vg = H.logical_kv(wl, type("L", (), {"k_pages": layer.k, "v_pages": layer.v}))
+    if not (np.array_equal(Kg, st.K) and np.array_equal(Vg, st.V)):
+        _fail("K/V caches differ after the appends")
+    for g in range(layer.NG):
+        C = int(st.num_comms[g])
+        a, b = rows[g, :C], st.cent[g, :C]
+        if not np.array_equal(a.view(np.uint32), b.view(np.uint32)):
+            na = np.linalg.norm((a - b).astype(np.float64), axis=-1)
+            nb = np.maximum(np.linalg.norm(b.astype(np.float64), axis=-1), 1e-30)
+            _fail(f"graph {g}: centroids differ, max relative norm error {float((na / nb).max()):.3e}")
+
+
+def run_parity(wl, steps=None, li=0, index_stride=None, log=print):
+    """Run `steps` decode steps of layer `li` on the GPU and in the oracle and
+    compare every step.  Returns a summary dict."""
+    steps = wl.steps if steps is None else steps
+    torch.cuda.synchronize()
+    layer = Bd.decode_layer_from_workload(wl, li, index_stride=index_stride)
+    st = H.oracle_state(wl, li)
+    L = wl.layers[li]
+    stats = []
+    t_gpu = t_ora = 0.0
+    for t in range(steps):
+        q, kn, vn = L.q[t].contiguous(), L.k_new[t].contiguous(), L.v_new[t].contiguous()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        layer.step(q, kn, vn, wl.scale)
+        torch.cuda.synchronize()
+        t_gpu += time.perf_counter() - t0
+        err = int(layer.err.item())
+        if err:
+            _fail(f"step {t}: device error flag {err}")
+        qh, knh, vnh = H.raw_np(q), H.raw_np(kn), H.raw_np(vn)
+        t0 = time.perf_counter()
+        res = st.step(qh, knh, vnh, wl.budget, wl.scale, wl.M, layer.index_list.shape[1])
+        t_ora += time.perf_counter() - t0
+        compare_step(layer, res, wl, t, stats)
+    compare_state(layer, st, wl)
+    mx = max(s[0] for s in stats)
+    rl = max(s[1] for s in stats)
+    summary = dict(steps=steps, max_abs=mx, max_rel_l2=rl, gpu_s=t_gpu, oracle_s=t_ora,
+                   mean_idx_len=float(layer.index_len.float().mean().item()))
+    log(f"parity ok: {summary}")
+    sys.stdout.flush()
+    return summary

@@ -1,0 +1,102 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, sizes workspaces, and rejects bad arguments before any HIP call.
+No call here passes validation, so nothing is ever launched."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from sparse_long_context_centroid_amd import binding as Bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ckv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(Bd.LIB_PATH):
+        from sparse_long_context_centroid_amd import build
+        build.build()
+    return Bd.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ckv_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = _declared()
+    assert set(decl) == set(Bd.EXPORTED), decl
+    out = os.popen(f"nm -D --defined-only {Bd.LIB_PATH}").read()
+    exported = set(re.findall(r"\bT (ckv_\w+)", out))
+    assert set(decl) <= exported
+    # nothing else leaks out of the library's C++ internals
+    assert not re.search(r"\bT _ZN3ckv", out)
+
+
+def dims(**kw):
+    d = dict(B=1, Hq=32, Hkv=8, d=128, gpk=1, Cmax=2048, S=4, dtype=Bd.CKV_DT_BF16)
+    d.update(kw)
+    return Bd.make_dims(d["B"], d["Hq"], d["Hkv"], d["d"], d["gpk"], d["Cmax"], d["S"],
+                        d["dtype"])
+
+
+def test_workspace_sizes(lib):
+    ok = dims(B=4)
+    # counters (NG u32, padded) + partials NG*G*splits*(d+2) fp32; 4100 entries -> 17 splits
+    ng, g, splits = 32, 4, (4100 + 255) // 256
+    expect = (ng * 4 + 255) // 256 * 256 + ng * g * splits * (128 + 2) * 4
+    assert lib.ckv_workspace_size(C.byref(ok), 4100) == expect
+    assert lib.ckv_score_workspace_size(C.byref(ok)) == ng * 4 * 128 * 8
+    assert lib.ckv_workspace_size(C.byref(dims(d=96)), 4100) == 0
+    assert lib.ckv_workspace_size(C.byref(ok), 0) == 0
+    assert lib.ckv_workspace_size(None, 16) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), -2), (dict(Hq=30), -1), (dict(Hq=48, Hkv=4), -2), (dict(gpk=2), -1),
+    (dict(Cmax=100), -1), (dict(Cmax=8192), -2), (dict(dtype=7), -2), (dict(B=0), -1),
+    (dict(S=-1), -1),
+])
+def test_bad_dims_rejected(lib, kw, status):
+    d = dims(**kw)
+    fake = C.c_void_p(0x1000)
+    g = Bd.ckv_graphs(fake, fake, fake, fake, fake, fake)
+    r = lib.ckv_score_centroids(C.byref(d), fake, C.byref(g), 0.1, fake, fake, 1 << 30, None)
+    assert r == status
+
+
+def test_null_pointers_and_small_workspace(lib):
+    d = dims()
+    fake = C.c_void_p(0x1000)
+    g = Bd.ckv_graphs(fake, fake, fake, fake, fake, None)           # members missing
+    assert lib.ckv_score_centroids(C.byref(d), fake, C.byref(g), 0.1, fake, fake, 1 << 30,
+                                   None) == -1
+    g = Bd.ckv_graphs(fake, fake, fake, fake, fake, fake)
+    assert lib.ckv_score_centroids(C.byref(d), fake, C.byref(g), 0.1, fake, fake, 16,
+                                   None) == -3
+    kv = Bd.ckv_kv(fake, fake, fake, 16, 8, 8, fake)
+    assert lib.ckv_sparse_decode_attn(C.byref(d), fake, C.byref(kv), fake, 2052, fake, 0.1,
+                                      fake, fake, 64, fake, None) == -3
+    kv_bad = Bd.ckv_kv(fake, fake, fake, 12, 8, 8, fake)             # page size not 2^k
+    assert lib.ckv_sparse_decode_attn(C.byref(d), fake, C.byref(kv_bad), fake, 2052, fake,
+                                      0.1, fake, fake, 1 << 30, fake, None) == -1
+    # select: n_cand out of range
+    assert lib.ckv_select(C.byref(d), fake, C.byref(g), fake, fake, 0, fake, 2052, fake, None,
+                          fake, None, fake, None) == -1
+    assert lib.ckv_select(C.byref(d), fake, C.byref(g), fake, fake, 17, fake, 2052, fake, None,
+                          fake, None, fake, None) == -1
+    assert lib.ckv_local_update(C.byref(d), fake, None, fake, 8, C.byref(g), C.byref(kv), fake,
+                                fake, None) == -1
+    assert lib.ckv_workspace_init(None, 16, None) == -1
+
+
+def test_status_strings(lib):
+    for s, txt in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported configuration"),
+                   (-3, "workspace missing or too small"), (-4, "HIP launch failed")]:
+        assert lib.ckv_status_string(s).decode() == txt

@@ -1,0 +1,143 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Sizes are chosen so that the oracle finishes in seconds while the kernels still
+span several tiles / splits and a ragged tail; the full-size cases run the
+configurations' real shapes for a few steps.  Every case prints its name first.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import brute
+import helpers as H
+from gpu_parity import run_parity
+from sparse_long_context_centroid_amd import binding as Bd
+from sparse_long_context_centroid_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    Bd.load()
+
+
+def _case(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+@pytest.mark.parametrize("cfg,kw", [
+    (0, dict()),
+    (1, dict(context=8192, steps=4)),
+    (2, dict(context=8192, steps=3)),
+    (3, dict(context=16384, steps=3)),
+    (4, dict(context=16384, steps=2, layers=2, batch=6)),
+])
+def test_parity_reduced(cfg, kw):
+    _case(f"cfg{cfg} {kw}")
+    wl = I.make_workload(cfg, device="cuda", **kw)
+    run_parity(wl, li=len(wl.layers) - 1)
+
+
+def test_parity_budget_zero_sinks_only():
+    _case("budget 0")
+    wl = I.make_workload(1, device="cuda", context=2048, steps=2, budget=0)
+    s = run_parity(wl)
+    assert s["mean_idx_len"] == wl.S
+
+
+def test_parity_full_budget_equals_dense():
+    _case("full budget == dense")
+    wl = I.make_workload(1, device="cuda", context=1536, steps=1, budget=1 << 20)
+    layer = Bd.decode_layer_from_workload(wl, 0, index_stride=2048)
+    L = wl.layers[0]
+    K, V = H.logical_kv(wl, L)
+    layer.step(L.q[0].contiguous(), L.k_new[0].contiguous(), L.v_new[0].contiguous(), wl.scale)
+    torch.cuda.synchronize()
+    assert int(layer.err.item()) == 0
+    out = layer.out.cpu().numpy()
+    q = H.raw_np(L.q[0])
+    n = int(wl.seq_len0[0])
+    assert (layer.index_len.cpu().numpy() == n).all()
+    for h in range(wl.Hq):
+        ref = brute.dense_attention(q[0, h], K[0, h // 4], V[0, h // 4], n, wl.scale)
+        assert np.max(np.abs(out[0, h] - ref.astype(np.float64))) < 2e-3
+
+
+def test_parity_single_candidate():
+    _case("M = 1")
+    wl = I.make_workload(1, device="cuda", context=4096, steps=3, n_cand=1)
+    run_parity(wl)
+
+
+def test_parity_exact_score_ties():
+    """Duplicated centroids give exactly equal scores; the (score desc, id asc)
+    order must be reproduced bit for bit."""
+    _case("tied scores")
+    wl = I.make_workload(1, device="cuda", context=4096, steps=3)
+    cen = wl.layers[0].centroids
+    C = int(wl.layers[0].num_comms.min())
+    cen[:, 1:C:2] = cen[:, 0:C - 1:2]
+    run_parity(wl)
+
+
+def test_parity_zero_query():
+    _case("q = 0")
+    wl = I.make_workload(1, device="cuda", context=4096, steps=2)
+    wl.layers[0].q.zero_()
+    run_parity(wl)
+
+
+def test_capacity_overflow_is_flagged():
+    _case("capacity overflow")
+    wl = I.make_workload(1, device="cuda", context=2048, steps=1, slack=0)
+    layer = Bd.decode_layer_from_workload(wl, 0)
+    L = wl.layers[0]
+    layer.step(L.q[0].contiguous(), L.k_new[0].contiguous(), L.v_new[0].contiguous(), wl.scale)
+    torch.cuda.synchronize()
+    assert int(layer.err.item()) & Bd.DEVERR_CAPACITY
+    assert (layer.assigned.cpu().numpy() == -1).all()
+    assert np.array_equal(layer.comm_size.cpu().numpy().reshape(L.comm_size.shape), L.comm_size)
+    assert (layer.seq_len.cpu().numpy() == wl.seq_len0 + 1).all()
+
+
+def test_unmapped_page_is_flagged_and_skipped():
+    _case("unmapped page")
+    wl = I.make_workload(1, device="cuda", context=2048, steps=1, budget=1 << 20)
+    layer = Bd.decode_layer_from_workload(wl, 0, index_stride=2048)
+    layer.page_table[0, 5] = -1      # tokens 80..95 become unreachable
+    L = wl.layers[0]
+    layer.step(L.q[0].contiguous(), L.k_new[0].contiguous(), L.v_new[0].contiguous(), wl.scale)
+    torch.cuda.synchronize()
+    assert int(layer.err.item()) & Bd.DEVERR_UNMAPPED_PAGE
+    K, V = H.logical_kv(wl, L)
+    q = H.raw_np(L.q[0])
+    keep = np.array([j for j in range(2048) if not 80 <= j < 96])
+    out = layer.out.cpu().numpy()
+    for h in (0, 13):
+        z =(brute.bf16_bits_to_ld(K[0, h // 4][keep]) @ brute.bf16_bits_to_ld(q[0, h])) \
+            * brute.LD(np.float32(wl.scale))
+        w = np.exp(z - z.max())
+        ref = (w[:, None] * brute.bf16_bits_to_ld(V[0, h // 4][keep])).sum(0) / w.sum()
+        assert np.max(np.abs(out[0, h] - ref.astype(np.float64))) < 2e-3
+
+
+@pytest.mark.parametrize("cfg,kw", [
+    (1, dict(steps=16)),
+    (2, dict(steps=8)),
+    (3, dict(steps=2)),
+])
+def test_parity_full_size(cfg, kw):
+    _case(f"full size cfg{cfg} {kw}")
+    wl = I.make_workload(cfg, device="cuda", **kw)
+    run_parity(wl)
+
+
+def test_parity_full_size_ragged_paged():
+    _case("full size cfg4, 1 of 36 layers")
+    wl = I.make_workload(4, device="cuda", steps=1, layers=1)
+    run_parity(wl)
