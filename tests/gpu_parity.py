@@ -106,7 +106,10 @@ def run_parity(wl, steps=None, li=0, index_stride=None, log=print):
     steps = wl.steps if steps is None else steps
     torch.cuda.synchronize()
     layer = Bd.decode_layer_from_workload(wl, li, index_stride=index_stride)
+    log(f"  device layer ready (NG={layer.NG}, Cmax={layer.Cmax})")
     st = H.oracle_state(wl, li)
+    log("  oracle state ready")
+    sys.stdout.flush()
     L = wl.layers[li]
     stats = []
     t_gpu = t_ora = 0.0
@@ -125,6 +128,9 @@ def run_parity(wl, steps=None, li=0, index_stride=None, log=print):
         res = st.step(qh, knh, vnh, wl.budget, wl.scale, wl.M, layer.index_list.shape[1])
         t_ora += time.perf_counter() - t0
         compare_step(layer, res, wl, t, stats)
+        if steps > 4:
+            log(f"  step {t + 1}/{steps} ok")
+            sys.stdout.flush()
     compare_state(layer, st, wl)
     mx = max(s[0] for s in stats)
     rl = max(s[1] for s in stats)
