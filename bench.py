@@ -7,9 +7,10 @@ Qwen3-8B-shaped attention layer, 4 sequences x 131072 tokens, 32 query / 8 KV
 heads, d = 128, bf16 K/V, query-group graphs with ~2048 communities per KV head,
 budget 4096 tokens + 4 sinks.
 
-Timing protocol (cold): before every timed step the script streams through a
-1 GiB scrub buffer so that neither the 4 MB L2s nor the 256 MB MALL hold the
-previous step's centroids, lists or KV rows; the step itself is bracketed by HIP
+Timing protocol (cold): before every timed step the script reads through a
+1 GiB scrub buffer (a reduction, so the caches end up holding clean scrub data)
+so that neither the 4 MB L2s nor the 256 MB MALL hold the previous step's
+centroids, lists or KV rows; the step itself is bracketed by HIP
 events on the stream the kernels run on, per kernel.  `value` = tokens (decode
 tokens of all sequences) / sum of the step times.  The warm back-to-back rate is
 reported beside it.  Inputs are resident in HBM before timing starts.
@@ -59,30 +60,26 @@ def step_bytes(layer: Bd.DecodeLayer, idx_len: np.ndarray, elem: int):
             rows += len(np.unique(np.concatenate([lists[g, :idx_len[g]] for g in gs])))
     else:
         rows = ntok
-    attn = rows * 2 * d * elem + ntok * 4 + Bq + layer.B * layer.Hq * d * 4
+    attn = rows * 2 * d * elem + ntok * 4 + Bq
     upd = layer.NG * (layer.M * d * 4 + layer.M * 4 + d * 4 * 2) + \
         layer.B * layer.Hkv * 2 * d * elem * 2
-    return dict(score=score, select=select, attn=attn, update=upd)
+    merge = layer.B * layer.Hq * d * 4
+    return dict(score=score, select_update=select + upd, attn=attn, merge=merge)
+
+
+KERNELS = ["score", "select_update", "attn", "merge"]
 
 
 class Timed:
-    """One layer's decode step with per-kernel HIP events."""
+    """One layer's fused decode step (ckv_decode_step, 4 kernels) with HIP events
+    recorded by the library between its kernels, on the stream they run on."""
 
     def __init__(self, layer):
         self.layer = layer
         self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
 
     def run(self, q, kn, vn, scale):
-        L, ev = self.layer, self.ev
-        ev[0].record()
-        L.score(q, scale)
-        ev[1].record()
-        L.select()
-        ev[2].record()
-        L.attend(q, scale)
-        ev[3].record()
-        L.update(kn, vn)
-        ev[4].record()
+        self.layer.step_fused(q, kn, vn, scale, events=self.ev)
 
     def times_ms(self):
         return [self.ev[i].elapsed_time(self.ev[i + 1]) for i in range(4)]
@@ -132,6 +129,9 @@ def main():
     ap.add_argument("--scrub-mib", type=int, default=1024)
     ap.add_argument("--warm", action="store_true", help="no cache scrub between steps")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before timing, run a plain device copy of this many MiB three times "
+                         "(a known-size kernel to calibrate hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -160,9 +160,16 @@ def main():
     timers = [Timed(l) for l in layers]
     elem = 2 if wl.dtype == I.DT_BF16 else 4
     scrub = torch.empty(args.scrub_mib << 18, dtype=torch.float32, device=dev).fill_(0.0)
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     qkv = [(L.q, L.k_new, L.v_new) for L in wl.layers]
     kernel_ms = np.zeros(4)
-    kernel_bytes = dict(score=0, select=0, attn=0, update=0)
+    kernel_bytes = {k: 0 for k in KERNELS}
     step_ms = []
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -171,7 +178,7 @@ def main():
         tot = 0.0
         for li, (tm, (q, kn, vn)) in enumerate(zip(timers, qkv)):
             if not args.warm:
-                scrub.add_(1.0)                       # cold caches, outside the events
+                scrub_sum = scrub.sum()               # cold caches, outside the events
             tm.run(q[t], kn[t], vn[t], wl.scale)
             torch.cuda.synchronize()
             if timed:
@@ -195,7 +202,7 @@ def main():
     toks = wl.B * K
     value = toks / (total_ms / 1e3)
     all_bytes = sum(kernel_bytes.values())
-    names = ["score", "select", "attn", "update"]
+    names = KERNELS
     per_kernel = {n: dict(ms_per_launch=kernel_ms[i] / (K * len(layers)),
                           gbs=kernel_bytes[n] / (kernel_ms[i] / 1e3) / 1e9 if kernel_ms[i] else None)
                   for i, n in enumerate(names)}
@@ -229,7 +236,7 @@ def main():
         "kernels": per_kernel,
         "wall_s_timed_loop": wall,
         "roofline": {
-            "kernel": "attn_kernel (indexed split-K flash-decode)",
+            "kernel": "attn_kernel (indexed split-K flash-decode, partials)",
             "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": attn_gbs / HBM_PEAK_GBS if attn_gbs else None, "traffic": None,
         },

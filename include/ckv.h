@@ -108,13 +108,10 @@ typedef struct ckv_kv {
     int32_t *seq_len;          /* [B] tokens in cache; ckv_local_update adds one     */
 } ckv_kv;
 
-/* Bytes of workspace ckv_sparse_decode_attn needs for index lists of up to
- * `index_stride` entries per graph.  Returns 0 for invalid dims. */
+/* Bytes of workspace ckv_sparse_decode_attn and ckv_decode_step need for index
+ * lists of up to `index_stride` entries per graph (split partials; no state is
+ * kept in it between calls).  Returns 0 for invalid dims. */
 CKV_API size_t ckv_workspace_size(const ckv_dims *dims, int32_t index_stride);
-
-/* Zero the workspace's arrival counters (a fill kernel, no memset node).  Call
- * once after allocating it; the kernels leave it zeroed after every call. */
-CKV_API ckv_status ckv_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Layout helpers: rows [NG][Cmax][d] fp32 <-> community-interleaved centroids. */
 CKV_API ckv_status ckv_centroids_from_rows(const ckv_dims *dims, const float *rows,
@@ -131,12 +128,10 @@ CKV_API ckv_status ckv_centroids_to_rows(const ckv_dims *dims, const float *cent
  * is empty.  Entries c >= num_comms[g] are not written.
  *   q      : [B][Hq][d] in dims.dtype
  *   scale  : usually 1/sqrt(d)
- *   q_ws   : device scratch of ckv_score_workspace_size(dims) bytes (fp64 copy of q)
  */
-CKV_API size_t ckv_score_workspace_size(const ckv_dims *dims);
-CKV_API ckv_status ckv_score_centroids(const ckv_dims *dims, const void *q, const ckv_graphs *graphs,
-                               float scale, float *scores, void *q_ws, size_t q_ws_bytes,
-                               void *stream);
+CKV_API ckv_status ckv_score_centroids(const ckv_dims *dims, const void *q,
+                                       const ckv_graphs *graphs, float scale, float *scores,
+                                       void *stream);
 
 /*
  * Budgeted community selection, sinks and compaction [RIT-granul: small active
@@ -168,8 +163,7 @@ CKV_API ckv_status ckv_select(const ckv_dims *dims, const float *scores, const c
  * over j in index_list[g*index_stride .. + index_len[g]), K/V rows read through
  * the page table.  fp32 accumulation, fp32 output; an empty list gives 0.
  * Entries outside [0, seq_len[b]) or on unmapped pages are skipped and flagged.
- * ws: ckv_workspace_size(dims, index_stride) bytes, zeroed once by
- * ckv_workspace_init.
+ * ws: ckv_workspace_size(dims, index_stride) bytes of scratch.
  */
 CKV_API ckv_status ckv_sparse_decode_attn(const ckv_dims *dims, const void *q, const ckv_kv *kv,
                                   const int32_t *index_list, int32_t index_stride,
@@ -193,6 +187,26 @@ CKV_API ckv_status ckv_local_update(const ckv_dims *dims, const void *k_new, con
                             const int32_t *cand, int32_t n_cand, const ckv_graphs *graphs,
                             const ckv_kv *kv, int32_t *assigned, int32_t *err_flag,
                             void *stream);
+
+/*
+ * One whole decode step, the four operations above in 4 kernel launches instead
+ * of 5: scoring; selection + compaction; sparse attention (split partials); and
+ * one launch that merges the partials (one workgroup per graph) and runs the
+ * local update with the seq_len advance (one workgroup per sequence).  Arguments
+ * and results are those of the four calls (num_selected and selected may be
+ * NULL), and every result equals the sequence
+ *   ckv_score_centroids; ckv_select; ckv_sparse_decode_attn; ckv_local_update.
+ * events: NULL, or 5 hipEvent_t (as void*) recorded on `stream` before the first
+ * kernel and after each of the 4 kernels, for per-kernel timing.
+ */
+CKV_API ckv_status ckv_decode_step(const ckv_dims *dims, const void *q, const void *k_new,
+                                   const void *v_new, const ckv_graphs *graphs, const ckv_kv *kv,
+                                   const int32_t *budget, int32_t n_cand, float scale,
+                                   float *scores, int32_t *index_list, int32_t index_stride,
+                                   int32_t *index_len, int32_t *num_selected, int32_t *cand,
+                                   uint8_t *selected, int32_t *assigned, float *out, void *ws,
+                                   size_t ws_bytes, int32_t *err_flag, void *const *events,
+                                   void *stream);
 
 CKV_API const char *ckv_status_string(ckv_status status);
 

@@ -61,14 +61,14 @@ def load(path: str = LIB_PATH):
     pd, pg, pk = C.POINTER(ckv_dims), C.POINTER(ckv_graphs), C.POINTER(ckv_kv)
     sig = {
         "ckv_workspace_size": (sz, [pd, i32]),
-        "ckv_workspace_init": (i32, [P, sz, P]),
         "ckv_centroids_from_rows": (i32, [pd, P, P, P]),
         "ckv_centroids_to_rows": (i32, [pd, P, P, P]),
-        "ckv_score_workspace_size": (sz, [pd]),
-        "ckv_score_centroids": (i32, [pd, P, pg, C.c_float, P, P, sz, P]),
+        "ckv_score_centroids": (i32, [pd, P, pg, C.c_float, P, P]),
         "ckv_select": (i32, [pd, P, pg, P, P, i32, P, i32, P, P, P, P, P, P]),
         "ckv_sparse_decode_attn": (i32, [pd, P, pk, P, i32, P, C.c_float, P, P, sz, P, P]),
         "ckv_local_update": (i32, [pd, P, P, P, i32, pg, pk, P, P, P]),
+        "ckv_decode_step": (i32, [pd, P, P, P, pg, pk, P, i32, C.c_float, P, P, i32, P, P, P,
+                                  P, P, P, P, sz, P, P, P]),
         "ckv_status_string": (C.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -79,9 +79,9 @@ def load(path: str = LIB_PATH):
     return L
 
 
-EXPORTED = ("ckv_workspace_size", "ckv_workspace_init", "ckv_centroids_from_rows",
-            "ckv_centroids_to_rows", "ckv_score_workspace_size", "ckv_score_centroids",
-            "ckv_select", "ckv_sparse_decode_attn", "ckv_local_update", "ckv_status_string")
+EXPORTED = ("ckv_workspace_size", "ckv_centroids_from_rows", "ckv_centroids_to_rows",
+            "ckv_score_centroids", "ckv_select", "ckv_sparse_decode_attn", "ckv_local_update",
+            "ckv_decode_step", "ckv_status_string")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -125,11 +125,6 @@ def ckv_workspace_size(dims: ckv_dims, index_stride: int) -> int:
     return load().ckv_workspace_size(C.byref(dims), index_stride)
 
 
-def ckv_workspace_init(ws: torch.Tensor, stream=None):
-    _check(load().ckv_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
-           "ckv_workspace_init")
-
-
 def ckv_centroids_from_rows(dims, rows, centroids, stream=None):
     _check(load().ckv_centroids_from_rows(C.byref(dims), _ptr(rows), _ptr(centroids),
                                           _stream(stream)), "ckv_centroids_from_rows")
@@ -140,14 +135,9 @@ def ckv_centroids_to_rows(dims, centroids, rows, stream=None):
                                         _stream(stream)), "ckv_centroids_to_rows")
 
 
-def ckv_score_workspace_size(dims: ckv_dims) -> int:
-    return load().ckv_score_workspace_size(C.byref(dims))
-
-
-def ckv_score_centroids(dims, q, graphs, scale, scores, q_ws, stream=None):
+def ckv_score_centroids(dims, q, graphs, scale, scores, stream=None):
     _check(load().ckv_score_centroids(C.byref(dims), _ptr(q), C.byref(graphs), scale,
-                                      _ptr(scores), _ptr(q_ws), q_ws.numel() * q_ws.element_size(),
-                                      _stream(stream)), "ckv_score_centroids")
+                                      _ptr(scores), _stream(stream)), "ckv_score_centroids")
 
 
 def ckv_select(dims, scores, graphs, budget, seq_len, n_cand, index_list, index_len,
@@ -171,6 +161,26 @@ def ckv_local_update(dims, k_new, v_new, cand, n_cand, graphs, kv, assigned, err
     _check(load().ckv_local_update(C.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(cand), n_cand,
                                    C.byref(graphs), C.byref(kv), _ptr(assigned), _ptr(err_flag),
                                    _stream(stream)), "ckv_local_update")
+
+
+def ckv_decode_step(dims, q, k_new, v_new, graphs, kv, budget, n_cand, scale, scores,
+                    index_list, index_len, num_selected, cand, selected, assigned, out, ws,
+                    err_flag, events=None, stream=None):
+    """events: None or 5 torch.cuda.Event(enable_timing=True), recorded before the
+    first kernel and after each of the 4 kernels."""
+    ev = None
+    if events is not None:
+        for e in events:
+            if e.cuda_event == 0:        # torch creates the HIP event at first record
+                e.record()
+        ev = (C.c_void_p * 5)(*[e.cuda_event for e in events])
+    _check(load().ckv_decode_step(C.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                  C.byref(graphs), C.byref(kv), _ptr(budget), n_cand, scale,
+                                  _ptr(scores), _ptr(index_list), index_list.shape[1],
+                                  _ptr(index_len), _ptr(num_selected), _ptr(cand),
+                                  _ptr(selected), _ptr(assigned), _ptr(out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _ptr(err_flag), ev,
+                                  _stream(stream)), "ckv_decode_step")
 
 
 def ckv_status_string(status: int) -> str:
@@ -213,8 +223,6 @@ class DecodeLayer:
         self.kv = make_kv(self.k, self.v, self.page_table, page_size, self.seq_len)
         # outputs and workspaces
         self.scores = torch.full((self.NG, Cmax), float("-inf"), dtype=torch.float32, device=dev)
-        self.q_ws = torch.empty(ckv_score_workspace_size(self.dims), dtype=torch.uint8,
-                                device=dev)
         self.index_list = torch.zeros((self.NG, index_stride), **i32)
         self.index_len = torch.zeros(self.NG, **i32)
         self.num_selected = torch.zeros(self.NG, **i32)
@@ -227,11 +235,10 @@ class DecodeLayer:
         if wsz == 0:
             raise CkvError("invalid dims for the workspace")
         self.ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
-        ckv_workspace_init(self.ws)
 
     # individual stages
     def score(self, q, scale):
-        ckv_score_centroids(self.dims, q, self.graphs, scale, self.scores, self.q_ws)
+        ckv_score_centroids(self.dims, q, self.graphs, scale, self.scores)
 
     def select(self):
         ckv_select(self.dims, self.scores, self.graphs, self.budget, self.seq_len, self.M,
@@ -247,10 +254,18 @@ class DecodeLayer:
                          self.assigned, self.err)
 
     def step(self, q, k_new, v_new, scale):
+        """The four calls of the C ABI, in order."""
         self.score(q, scale)
         self.select()
         self.attend(q, scale)
         self.update(k_new, v_new)
+
+    def step_fused(self, q, k_new, v_new, scale, events=None):
+        """The same step through ckv_decode_step (4 launches)."""
+        ckv_decode_step(self.dims, q, k_new, v_new, self.graphs, self.kv, self.budget, self.M,
+                        scale, self.scores, self.index_list, self.index_len, self.num_selected,
+                        self.cand, self.selected, self.assigned, self.out, self.ws, self.err,
+                        events=events)
 
     def centroid_rows(self) -> torch.Tensor:
         rows = torch.empty((self.NG, self.Cmax, self.d), dtype=torch.float32,

@@ -42,15 +42,24 @@ ckv_status check_graphs(const ckv_graphs *g) {
     return CKV_OK;
 }
 
-ckv_status check_kv(const ckv_kv *kv) {
+ckv_status check_kv(const ckv_kv *kv, const Problem &p) {
     if (!kv || !kv->k || !kv->v || !kv->page_table || !kv->seq_len) return CKV_ERR_INVALID_ARG;
     if (!is_pow2(kv->page_size) || kv->page_size > 4096 || kv->max_pages_per_seq < 1 ||
         kv->num_pages < 1)
         return CKV_ERR_INVALID_ARG;
+    // row indices (page, head, slot) are 32-bit inside the kernels
+    if ((long long)kv->num_pages * p.Hkv * kv->page_size >= (1LL << 31))
+        return CKV_ERR_UNSUPPORTED;
     return CKV_OK;
 }
 
 ckv_status hip_status(hipError_t e) { return e == hipSuccess ? CKV_OK : CKV_ERR_HIP; }
+
+// The split merge keeps one weight per (head, split) in LDS.
+ckv_status check_splits(const Problem &p, int index_stride) {
+    const size_t lds = (size_t)p.heads_per_graph() * ckv::attn_max_splits(p, index_stride) * 4;
+    return lds <= 65536 ? CKV_OK : CKV_ERR_UNSUPPORTED;
+}
 
 }  // namespace
 
@@ -59,12 +68,7 @@ extern "C" {
 size_t ckv_workspace_size(const ckv_dims *dims, int32_t index_stride) {
     Problem p;
     if (make_problem(dims, p) != CKV_OK || index_stride < 1) return 0;
-    return ckv::attn_counter_bytes(p) + ckv::attn_partial_floats(p, index_stride) * sizeof(float);
-}
-
-ckv_status ckv_workspace_init(void *ws, size_t ws_bytes, void *stream) {
-    if (!ws || ws_bytes == 0) return CKV_ERR_INVALID_ARG;
-    return hip_status(ckv::launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)));
+    return ckv::attn_partial_floats(p, index_stride) * sizeof(float);
 }
 
 ckv_status ckv_centroids_from_rows(const ckv_dims *dims, const float *rows, float *centroids,
@@ -87,25 +91,15 @@ ckv_status ckv_centroids_to_rows(const ckv_dims *dims, const float *centroids, f
                                                        static_cast<hipStream_t>(stream)));
 }
 
-size_t ckv_score_workspace_size(const ckv_dims *dims) {
-    Problem p;
-    if (make_problem(dims, p) != CKV_OK) return 0;
-    return (size_t)p.NG() * p.heads_per_graph() * p.D * sizeof(double);
-}
-
 ckv_status ckv_score_centroids(const ckv_dims *dims, const void *q, const ckv_graphs *graphs,
-                               float scale, float *scores, void *q_ws, size_t q_ws_bytes,
-                               void *stream) {
+                               float scale, float *scores, void *stream) {
     Problem p;
     ckv_status s = make_problem(dims, p);
     if (s != CKV_OK) return s;
     if ((s = check_graphs(graphs)) != CKV_OK) return s;
     if (!q || !scores) return CKV_ERR_INVALID_ARG;
-    if (!q_ws || q_ws_bytes < ckv_score_workspace_size(dims)) return CKV_ERR_WORKSPACE;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    double *q64 = static_cast<double *>(q_ws);
-    if ((s = hip_status(ckv::launch_stage_query(p, q, q64, st))) != CKV_OK) return s;
-    return hip_status(ckv::launch_score(p, q64, *graphs, (double)scale, scores, st));
+    return hip_status(ckv::launch_score(p, q, *graphs, (double)scale, scores,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 ckv_status ckv_select(const ckv_dims *dims, const float *scores, const ckv_graphs *graphs,
@@ -132,15 +126,17 @@ ckv_status ckv_sparse_decode_attn(const ckv_dims *dims, const void *q, const ckv
     Problem p;
     ckv_status s = make_problem(dims, p);
     if (s != CKV_OK) return s;
-    if ((s = check_kv(kv)) != CKV_OK) return s;
+    if ((s = check_kv(kv, p)) != CKV_OK) return s;
     if (!q || !index_list || !index_len || !out || index_stride < 1) return CKV_ERR_INVALID_ARG;
-    const size_t need = ckv_workspace_size(dims, index_stride);
-    if (!ws || ws_bytes < need) return CKV_ERR_WORKSPACE;
-    uint32_t *counters = static_cast<uint32_t *>(ws);
-    float *partials = reinterpret_cast<float *>(static_cast<char *>(ws) + ckv::attn_counter_bytes(p));
-    return hip_status(ckv::launch_attn(p, q, *kv, index_list, index_stride, index_len, scale, out,
-                                       counters, partials, err_flag,
-                                       static_cast<hipStream_t>(stream)));
+    if ((s = check_splits(p, index_stride)) != CKV_OK) return s;
+    if (!ws || ws_bytes < ckv_workspace_size(dims, index_stride)) return CKV_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((s = hip_status(ckv::launch_attn_partials(p, q, *kv, index_list, index_stride, index_len,
+                                                  scale, static_cast<float *>(ws), err_flag,
+                                                  st))) != CKV_OK)
+        return s;
+    return hip_status(ckv::launch_attn_merge(p, index_len, index_stride, out,
+                                             static_cast<float *>(ws), st));
 }
 
 ckv_status ckv_local_update(const ckv_dims *dims, const void *k_new, const void *v_new,
@@ -151,11 +147,56 @@ ckv_status ckv_local_update(const ckv_dims *dims, const void *k_new, const void 
     ckv_status s = make_problem(dims, p);
     if (s != CKV_OK) return s;
     if ((s = check_graphs(graphs)) != CKV_OK) return s;
-    if ((s = check_kv(kv)) != CKV_OK) return s;
+    if ((s = check_kv(kv, p)) != CKV_OK) return s;
     if (!k_new || !v_new || !cand || !assigned) return CKV_ERR_INVALID_ARG;
     if (n_cand < 1 || n_cand > CKV_MAX_CAND) return CKV_ERR_INVALID_ARG;
     return hip_status(ckv::launch_update(p, k_new, v_new, cand, n_cand, *graphs, *kv, assigned,
                                          err_flag, static_cast<hipStream_t>(stream)));
+}
+
+ckv_status ckv_decode_step(const ckv_dims *dims, const void *q, const void *k_new,
+                           const void *v_new, const ckv_graphs *graphs, const ckv_kv *kv,
+                           const int32_t *budget, int32_t n_cand, float scale, float *scores,
+                           int32_t *index_list, int32_t index_stride, int32_t *index_len,
+                           int32_t *num_selected, int32_t *cand, uint8_t *selected,
+                           int32_t *assigned, float *out, void *ws, size_t ws_bytes,
+                           int32_t *err_flag, void *const *events, void *stream) {
+    Problem p;
+    ckv_status s = make_problem(dims, p);
+    if (s != CKV_OK) return s;
+    if ((s = check_graphs(graphs)) != CKV_OK) return s;
+    if ((s = check_kv(kv, p)) != CKV_OK) return s;
+    if (!q || !k_new || !v_new || !budget || !scores || !index_list || !index_len || !cand ||
+        !assigned || !out)
+        return CKV_ERR_INVALID_ARG;
+    if (n_cand < 1 || n_cand > CKV_MAX_CAND || index_stride < 1) return CKV_ERR_INVALID_ARG;
+    if ((s = check_splits(p, index_stride)) != CKV_OK) return s;
+    if (!ws || ws_bytes < ckv_workspace_size(dims, index_stride)) return CKV_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) -> ckv_status {
+        if (!events) return CKV_OK;
+        return hip_status(hipEventRecord(static_cast<hipEvent_t>(events[i]), st));
+    };
+    if ((s = mark(0)) != CKV_OK) return s;
+    if ((s = hip_status(ckv::launch_score(p, q, *graphs, (double)scale, scores, st))) != CKV_OK)
+        return s;
+    if ((s = mark(1)) != CKV_OK) return s;
+    if ((s = hip_status(ckv::launch_select(p, scores, *graphs, budget, kv->seq_len, n_cand,
+                                           index_list, index_stride, index_len, num_selected,
+                                           cand, selected, err_flag, st))) != CKV_OK)
+        return s;
+    if ((s = mark(2)) != CKV_OK) return s;
+    if ((s = hip_status(ckv::launch_attn_partials(p, q, *kv, index_list, index_stride, index_len,
+                                                  scale, static_cast<float *>(ws), err_flag,
+                                                  st))) != CKV_OK)
+        return s;
+    if ((s = mark(3)) != CKV_OK) return s;
+    if ((s = hip_status(ckv::launch_merge_update(p, index_len, index_stride, out,
+                                                 static_cast<float *>(ws), k_new, v_new, cand,
+                                                 n_cand, *graphs, *kv, assigned, err_flag, st))) !=
+        CKV_OK)
+        return s;
+    return mark(4);
 }
 
 const char *ckv_status_string(ckv_status status) {

@@ -1,4 +1,5 @@
-// attn.hip -- indexed split-K flash-decode over the selected tokens.
+// attn.hip -- indexed split-K flash-decode over the selected tokens, and the
+// log-sum-exp merge of the splits.
 //
 // rit.work post "CommunityKV long-context decoding", token-graph section: the
 // chosen communities are loaded from the full (never evicted) KV cache and
@@ -7,22 +8,31 @@
 //   o_h = sum_{j in I_g} exp(z_j - max z) V_j / sum_{j in I_g} exp(z_j - max z),
 //   z_j = scale * q_h . K_j.
 //
-// gfx950 design (VALU path):
-// * One workgroup = 4 wavefronts = 4*16*RPW consecutive entries (256 for bf16
-//   d=128) of one
-//   graph's index list; grid = (max splits, NG); workgroups past the list exit.
-// * A K or V row (d*elem bytes = 256 B for bf16 d=128 or fp32 d=64) is read by
-//   LPR = row_bytes/16 lanes with one 16-byte load each, so one wave-wide load
-//   gathers 64/LPR whole rows (1 KiB) -- coalesced row gathers through the page
-//   table.  All 2*(64/RPW) loads of a wave are issued before any arithmetic.
-// * Logits are reduced over the LPR lanes of a row with DPP adds; softmax runs in
-//   the log2 domain in fp32; each wave keeps (m, l, acc) per head, the 4 waves are
-//   merged in LDS and the workgroup writes one partial (m, l, acc[d]) per head.
-// * The last workgroup of a graph to finish (device-scope arrival counter) merges
-//   the partials with the log-sum-exp rule and writes the fp32 output, then resets
-//   the counter -- no second launch.
+// gfx950 design (VALU path; per token the group's 4 heads need 2*4*d FMAs on
+// 2*d*2 bytes, ~2 FMA/B, below the fp32 vector ridge):
+// * grid = (NG, splits): the graph index varies fastest, so the workgroups of one
+//   graph share an XCD (and its L2) and the short last splits are dispatched last;
+//   a graph's list is cut into `nsplit` balanced chunks of <= CH entries.
+// * Phase A: each thread resolves one list entry -> page-table lookup -> row index
+//   (or -1 when out of range / unmapped), into LDS.
+// * Phase B: a K or V row (d*elem bytes, 256 B for bf16 d=128) is read by LPR =
+//   row_bytes/16 lanes with one 16-byte load each, so a wave-wide load gathers
+//   64/LPR whole rows (1 KiB); every wave issues its 2*NLD loads back to back with
+//   no branches (rows of invalid entries point at row 0 and are masked).
+// * q.K: bf16 pairs go straight into v_dot2_f32_bf16 (exact bf16 products, fp32
+//   sums), partial sums are reduced over the LPR lanes of a row with DPP adds.
+//   Softmax runs online (one rescale per 2 loads) in the log2 domain in fp32, so
+//   no logits are kept and a lane holds only its 2*NLD loads, q and acc: with
+//   NLD = 12 the kernel fits 3 waves per SIMD and a 128K-token step's whole K/V
+//   working set is requested in one round of workgroups.  The wave's row slots and
+//   then the 4 waves are merged; the workgroup writes one partial (m, l, acc[d])
+//   per head.
+// * The merge (next launch, so no device-wide fences are needed) combines the
+//   partials: m* = max m_s, l = sum l_s 2^(m_s-m*), o = sum acc_s 2^(m_s-m*) / l.
+//   In the fused decode step the same launch also runs the local update.
 #include "ckv_device.h"
 #include "ckv_internal.h"
+#include "update_rule.h"
 
 namespace ckv {
 
@@ -44,30 +54,78 @@ __device__ __forceinline__ void unpack<float, 4>(const uint4 &u, float (&x)[4]) 
     x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
 }
 
+// Graph handled by grid column x: for per-head graphs whose count is a multiple of
+// 8*gpk, the gpk graphs of a KV head are placed on one XCD (x % 8) so that their
+// overlapping lists hit the same L2.
+__device__ __forceinline__ int graph_of_column(int x, int NG, int gpk) {
+    if (gpk > 1 && NG % (8 * gpk) == 0) {
+        const int xcd = x & 7, rest = x >> 3;
+        return ((rest / gpk) * 8 + xcd) * gpk + rest % gpk;
+    }
+    return x;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Partial q.K over this lane's EPL elements of a row, for one head.
+template <typename T, int EPL>
+__device__ __forceinline__ float qk_part(const uint32_t (&qp)[EPL / 2 > 0 ? EPL / 2 : 1],
+                                         const float (&qf)[EPL], const uint4 &k);
+
+template <>
+__device__ __forceinline__ float qk_part<bf16_t, 8>(const uint32_t (&qp)[4], const float (&)[8],
+                                                    const uint4 &k) {
+    // bf16 x bf16 products are exact in fp32; v_dot2 accumulates two per step
+    float s = 0.f;
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[0]),
+                                        __builtin_bit_cast(bf16x2_t, k.x), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[1]),
+                                        __builtin_bit_cast(bf16x2_t, k.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[2]),
+                                        __builtin_bit_cast(bf16x2_t, k.z), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[3]),
+                                        __builtin_bit_cast(bf16x2_t, k.w), s, false);
+    return s;
+}
+
+template <>
+__device__ __forceinline__ float qk_part<float, 4>(const uint32_t (&)[2], const float (&qf)[4],
+                                                   const uint4 &k) {
+    float s = 0.f;
+    s = fmaf(qf[0], __uint_as_float(k.x), s);
+    s = fmaf(qf[1], __uint_as_float(k.y), s);
+    s = fmaf(qf[2], __uint_as_float(k.z), s);
+    s = fmaf(qf[3], __uint_as_float(k.w), s);
+    return s;
+}
+
 template <typename T, int D, int GH>
 __global__ __launch_bounds__(256) void attn_kernel(
     const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
     const int32_t *__restrict__ page_table, int log2ps, int max_pages, int num_pages,
     const int32_t *__restrict__ seq_len, const int32_t *__restrict__ idx, int idx_stride,
     const int32_t *__restrict__ idx_len, int Hq, int Hkv, int gpk, float scale_log2,
-    float *__restrict__ out, uint32_t *__restrict__ counters, float *__restrict__ part,
-    int max_splits, int32_t *__restrict__ err) {
-    constexpr int EPL = 16 / sizeof(T);      // row elements per lane
-    constexpr int LPR = D / EPL;             // lanes per row
-    constexpr int RPW = kWave / LPR;         // rows per wave-wide load
-    constexpr int NLD = kAttnLoads;          // loads per wave for K (and for V)
-    constexpr int kTokPerWave = NLD * RPW;
-    constexpr int kChunk = kTokPerWave * kAttnWaves;
-    static_assert(kChunk == attn_chunk(D, sizeof(T)), "chunk");
+    float *__restrict__ part, int max_splits, int32_t *__restrict__ err) {
+    constexpr int EPL = 16 / sizeof(T);     // row elements per lane
+    constexpr int LPR = D / EPL;            // lanes per row
+    constexpr int RPW = kWave / LPR;        // rows per wave-wide load
+    constexpr int NLD = kAttnLoads;         // loads per wave for K (and for V)
+    constexpr int TPW = NLD * RPW;          // tokens per wave
+    constexpr int CH = TPW * kAttnWaves;    // tokens per workgroup (max)
+    constexpr int NQP = EPL / 2 > 0 ? EPL / 2 : 1;
+    constexpr int kSub = 2;                 // loads per online-softmax batch
+    static_assert(CH == attn_chunk(D, sizeof(T)), "chunk");
     static_assert(LPR >= 1 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "row split");
+    static_assert(NLD % 4 == 0 && NLD % kSub == 0, "row slots are read as int4");
 
+    __shared__ __align__(16) int s_row[CH];
     __shared__ float s_m[kAttnWaves][GH];
     __shared__ float s_l[kAttnWaves][GH];
     __shared__ float s_acc[kAttnWaves][GH][D];
-    __shared__ int s_last;
 
-    const int split = blockIdx.x;
-    const int g = blockIdx.y;
+    const int NG = gridDim.x;
+    const int g = graph_of_column(blockIdx.x, NG, gpk);
+    const int split = blockIdx.y;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
@@ -76,116 +134,134 @@ __global__ __launch_bounds__(256) void attn_kernel(
     const int kvh = (g / gpk) % Hkv;
     const int h0 = kvh * G + (gpk == 1 ? 0 : g % gpk);
     const int len = min(idx_len[g], idx_stride);
-    const int nsplit = (len + kChunk - 1) / kChunk;
-
-    if (len <= 0) {
-        if (split == 0)
-            for (int t = tid; t < GH * D; t += blockDim.x)
-                out[((size_t)b * Hq + h0 + t / D) * D + t % D] = 0.f;
-        return;
-    }
+    const int nsplit = (len + CH - 1) / CH;
     if (split >= nsplit) return;
-
+    // balanced cut of the list into nsplit chunks
+    const int t_begin = (int)(((long long)len * split) / nsplit);
+    const int t_end = (int)(((long long)len * (split + 1)) / nsplit);
     const int n = seq_len[b];
     const int ls = lane % LPR;  // slice of the row this lane reads
     const int rs = lane / LPR;  // row slot inside a wave-wide load
 
-    // query slice, pre-scaled into the log2 domain
-    float qv[GH][EPL];
+    // query slice: packed bf16 pairs (dot2) or fp32; the scale is applied to the sum
+    uint32_t qp[GH][NQP];
+    float qf[GH][EPL];
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(q + ((size_t)b * Hq + h0 + h) * D + ls * EPL);
-        float x[EPL];
-        unpack<T, EPL>(u, x);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) qv[h][e] = x[e] * scale_log2;
-    }
-
-    // this wave's tokens: entries t0 .. t0+63 of the list
-    const int t0 = split * kChunk + w * kTokPerWave;
-    const int te = t0 + lane;
-    size_t rowoff = 0;
-    bool ok = false;
-    if (te < len) {
-        const int pos = idx[(size_t)g * idx_stride + te];
-        if (pos >= 0 && pos < n) {
-            const int lp = pos >> log2ps;
-            const int pg = lp < max_pages ? page_table[(size_t)b * max_pages + lp] : -1;
-            if (pg >= 0 && pg < num_pages) {
-                rowoff = ((((size_t)pg * Hkv + kvh) << log2ps) + (pos & ((1 << log2ps) - 1))) * D;
-                ok = true;
-            } else {
-                set_err(err, CKV_DEVERR_UNMAPPED_PAGE);
-            }
+        const uint4 u =
+            *reinterpret_cast<const uint4 *>(q + ((size_t)b * Hq + h0 + h) * D + ls * EPL);
+        if constexpr (sizeof(T) == 2) {
+            qp[h][0] = u.x; qp[h][1] = u.y; qp[h][2] = u.z; qp[h][3] = u.w;
         } else {
-            set_err(err, CKV_DEVERR_INDEX_RANGE);
+            qf[h][0] = __uint_as_float(u.x); qf[h][1] = __uint_as_float(u.y);
+            qf[h][2] = __uint_as_float(u.z); qf[h][3] = __uint_as_float(u.w);
         }
     }
 
+    // ---- phase A: list entries -> row indices in LDS
+    for (int t = tid; t < CH; t += blockDim.x) {
+        const int te = t_begin + t;
+        int row = -1;
+        if (te < t_end) {
+            const int pos = idx[(size_t)g * idx_stride + te];
+            if (pos >= 0 && pos < n) {
+                const int lp = pos >> log2ps;
+                const int pg = lp < max_pages ? page_table[(size_t)b * max_pages + lp] : -1;
+                if (pg >= 0 && pg < num_pages)
+                    row = ((pg * Hkv + kvh) << log2ps) + (pos & ((1 << log2ps) - 1));
+                else
+                    set_err(err, CKV_DEVERR_UNMAPPED_PAGE);
+            } else {
+                set_err(err, CKV_DEVERR_INDEX_RANGE);
+            }
+        }
+        s_row[t] = row;
+    }
+    __syncthreads();
+
+    // ---- phase B: this lane's NLD row slots are contiguous in LDS
+    int rows[NLD];
+    {
+        const int4 *sr = reinterpret_cast<const int4 *>(s_row + w * TPW + rs * NLD);
+#pragma unroll
+        for (int i = 0; i < NLD / 4; ++i) {
+            const int4 r4 = sr[i];
+            rows[4 * i + 0] = r4.x;
+            rows[4 * i + 1] = r4.y;
+            rows[4 * i + 2] = r4.z;
+            rows[4 * i + 3] = r4.w;
+        }
+    }
+    uint32_t valid = 0;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) valid |= (rows[i] >= 0 ? 1u : 0u) << i;
     uint4 kr[NLD], vr[NLD];
-    bool okr[NLD];
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-        const int src = i * RPW + rs;
-        const size_t ro = (size_t)__shfl((long long)rowoff, src);
-        okr[i] = __shfl((int)ok, src) != 0;
-        kr[i] = okr[i] ? *reinterpret_cast<const uint4 *>(kc + ro + ls * EPL) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < NLD; ++i)
+        kr[i] = *reinterpret_cast<const uint4 *>(kc + (size_t)(rows[i] < 0 ? 0 : rows[i]) * D +
+                                                 ls * EPL);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-        const int src = i * RPW + rs;
-        const size_t ro = (size_t)__shfl((long long)rowoff, src);
-        vr[i] = okr[i] ? *reinterpret_cast<const uint4 *>(vc + ro + ls * EPL) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < NLD; ++i)
+        vr[i] = *reinterpret_cast<const uint4 *>(vc + (size_t)(rows[i] < 0 ? 0 : rows[i]) * D +
+                                                 ls * EPL);
 
-    // logits (log2 domain), one per (load, head); identical on the LPR lanes of a row
-    float z[NLD][GH];
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-        float x[EPL];
-        unpack<T, EPL>(kr[i], x);
-#pragma unroll
-        for (int h = 0; h < GH; ++h) {
-            float s = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) s = fmaf(qv[h][e], x[e], s);
-            s = group_sum<LPR>(s);
-            z[i][h] = okr[i] ? s : -__builtin_inff();
-        }
-    }
-    // wave-wide max per head
-    float m[GH];
+    // online softmax over batches of kSub loads; m, l, acc are per row slot
+    float m[GH], l[GH], acc[GH][EPL];
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
-        float mm = -__builtin_inff();
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) mm = fmaxf(mm, z[i][h]);
-#pragma unroll
-        for (int off = LPR; off < kWave; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
-        m[h] = mm;
-    }
-    float l[GH], acc[GH][EPL];
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
+        m[h] = -__builtin_inff();
         l[h] = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-        float x[EPL];
-        unpack<T, EPL>(vr[i], x);
+    for (int i0 = 0; i0 < NLD; i0 += kSub) {
+        float z[kSub][GH];
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+#pragma unroll
+            for (int h = 0; h < GH; ++h) {
+                const float s = group_sum<LPR>(qk_part<T, EPL>(qp[h], qf[h], kr[i0 + j]));
+                z[j][h] = (valid >> (i0 + j)) & 1u ? s * scale_log2 : -__builtin_inff();
+            }
+        }
 #pragma unroll
         for (int h = 0; h < GH; ++h) {
-            const float p = okr[i] ? fast_exp2(z[i][h] - m[h]) : 0.f;
-            l[h] += p;
+            float mn = m[h];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
+            for (int j = 0; j < kSub; ++j) mn = fmaxf(mn, z[j][h]);
+            if (mn != -__builtin_inff()) {
+                const float c = fast_exp2(m[h] - mn);  // 0 when m was -inf
+                l[h] *= c;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[h][e] *= c;
+                m[h] = mn;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            float x[EPL];
+            unpack<T, EPL>(vr[i0 + j], x);
+#pragma unroll
+            for (int h = 0; h < GH; ++h) {
+                const float p = (valid >> (i0 + j)) & 1u ? fast_exp2(z[j][h] - m[h]) : 0.f;
+                l[h] += p;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
+            }
         }
     }
-    // merge the RPW row slots of the wave (same dims, disjoint tokens, same m)
+    // merge the RPW row slots of the wave (same dims, disjoint tokens, own maxima)
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
+        float mm = m[h];
+#pragma unroll
+        for (int off = LPR; off < kWave; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
+        const float c = mm == -__builtin_inff() ? 0.f : fast_exp2(m[h] - mm);
+        l[h] *= c;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= c;
+        m[h] = mm;
 #pragma unroll
         for (int off = LPR; off < kWave; off <<= 1) {
             l[h] += __shfl_xor(l[h], off);
@@ -227,56 +303,134 @@ __global__ __launch_bounds__(256) void attn_kernel(
             pp[1] = ll;
         }
     }
+}
 
-    // last workgroup of this graph merges all partials
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(&counters[g], 1u);
-        s_last = (prev == (uint32_t)(nsplit - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int t = tid; t < GH * D; t += blockDim.x) {
-        const int h = t / D, i = t % D;
+// Merge of one graph's split partials into out.  The per-split weights
+// 2^(m_s - m*) / l are formed once in LDS (s_w, GH*max_splits floats); every output
+// element then sums its nsplit partial values with all loads of a batch in flight.
+template <int D, int GH>
+__device__ __forceinline__ void merge_graph(int g, const int32_t *__restrict__ idx_len, int idx_stride, int chunk,
+                            int Hq, int Hkv, int gpk, float *__restrict__ out,
+                            const float *__restrict__ part, int max_splits, float *s_w) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    const int G = Hq / Hkv;
+    const int b = g / (Hkv * gpk);
+    const int kvh = (g / gpk) % Hkv;
+    const int h0 = kvh * G + (gpk == 1 ? 0 : g % gpk);
+    const int len = min(idx_len[g], idx_stride);
+    const int nsplit = (len + chunk - 1) / chunk;
+    const float *pbase = part + ((size_t)g * GH * max_splits) * (D + 2);
+    for (int h = w; h < GH; h += blockDim.x / kWave) {  // weights: one wave per head
         const float *ph = pbase + (size_t)h * max_splits * (D + 2);
         float mm = -__builtin_inff();
-        for (int s = 0; s < nsplit; ++s) mm = fmaxf(mm, __builtin_nontemporal_load(ph + (size_t)s * (D + 2)));
-        float a = 0.f, ll = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const float ms = __builtin_nontemporal_load(ph + (size_t)s * (D + 2));
+        for (int s = lane; s < nsplit; s += kWave) mm = fmaxf(mm, ph[(size_t)s * (D + 2)]);
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
+        float ll = 0.f;
+        for (int s = lane; s < nsplit; s += kWave) {
+            const float ms = ph[(size_t)s * (D + 2)];
             const float f = ms == -__builtin_inff() ? 0.f : fast_exp2(ms - mm);
-            ll += __builtin_nontemporal_load(ph + (size_t)s * (D + 2) + 1) * f;
-            a += __builtin_nontemporal_load(ph + (size_t)s * (D + 2) + 2 + i) * f;
+            s_w[h * max_splits + s] = f;
+            ll += ph[(size_t)s * (D + 2) + 1] * f;
         }
-        out[((size_t)b * Hq + h0 + h) * D + i] = ll > 0.f ? a / ll : 0.f;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) ll += __shfl_xor(ll, off);
+        const float inv = ll > 0.f ? 1.f / ll : 0.f;
+        for (int s = lane; s < nsplit; s += kWave) s_w[h * max_splits + s] *= inv;
     }
-    if (tid == 0) counters[g] = 0u;
+    __syncthreads();
+    constexpr int kBatch = 16;
+    for (int t = tid; t < GH * D; t += blockDim.x) {
+        const int h = t / D, i = t % D;
+        const float *ph = pbase + (size_t)h * max_splits * (D + 2) + 2 + i;
+        float a = 0.f;
+        for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+            float x[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                x[k] = s0 + k < nsplit ? ph[(size_t)(s0 + k) * (D + 2)] : 0.f;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                if (s0 + k < nsplit) a += x[k] * s_w[h * max_splits + s0 + k];
+        }
+        out[((size_t)b * Hq + h0 + h) * D + i] = a;
+    }
+}
+
+template <int D, int GH>
+__global__ __launch_bounds__(512) void merge_kernel(const int32_t *__restrict__ idx_len,
+                                                    int idx_stride, int chunk, int Hq, int Hkv,
+                                                    int gpk, float *__restrict__ out,
+                                                    const float *__restrict__ part,
+                                                    int max_splits) {
+    extern __shared__ float s_w[];
+    merge_graph<D, GH>(blockIdx.x, idx_len, idx_stride, chunk, Hq, Hkv, gpk, out, part,
+                       max_splits, s_w);
+}
+
+// Fused decode step, last kernel: workgroups 0..NG-1 merge the partials of graph
+// x; workgroups NG..NG+B-1 run the local update of sequence x-NG (every graph of
+// it, then seq_len += 1).  Attention has finished reading rows < n, so the update
+// may append row n here.
+struct UpdateArgs {
+    const void *k_new, *v_new;
+    const int32_t *cand;
+    int M;
+    float *cent;
+    const int32_t *num_comms, *comm_start;
+    int32_t *comm_size;
+    const int32_t *comm_cap;
+    int32_t *members;
+    int Cmax;
+    void *kc, *vc;
+    const int32_t *page_table;
+    int log2ps, max_pages, num_pages;
+    int32_t *seq_len, *assigned, *err;
+};
+
+template <typename T, int D, int GH>
+__global__ __launch_bounds__(512) void merge_update_kernel(const int32_t *__restrict__ idx_len,
+                                                           int idx_stride, int chunk, int Hq,
+                                                           int Hkv, int gpk, int NG,
+                                                           float *__restrict__ out,
+                                                           const float *__restrict__ part,
+                                                           int max_splits, UpdateArgs u) {
+    extern __shared__ float s_w[];
+    __shared__ __align__(16) float s_rows[(512 / kWave) * 3 * D];
+    if ((int)blockIdx.x < NG) {
+        merge_graph<D, GH>(blockIdx.x, idx_len, idx_stride, chunk, Hq, Hkv, gpk, out, part,
+                           max_splits, s_w);
+        return;
+    }
+    sequence_update<T, D>(blockIdx.x - NG, static_cast<const T *>(u.k_new),
+                          static_cast<const T *>(u.v_new), u.cand, u.M, u.cent, u.num_comms,
+                          u.comm_start, u.comm_size, u.comm_cap, u.members, u.Cmax, Hkv, gpk,
+                          static_cast<T *>(u.kc), static_cast<T *>(u.vc), u.page_table, u.log2ps,
+                          u.max_pages, u.num_pages, u.seq_len, u.assigned, u.err, s_rows);
 }
 
 template <typename T, int D, int GH>
-static void launch_attn_t(const Problem &p, const void *q, const ckv_kv &kv, const int32_t *idx,
-                          int idx_stride, const int32_t *idx_len, float scale, float *out,
-                          uint32_t *counters, float *partials, int32_t *err, hipStream_t st) {
-    int log2ps = 0;
-    while ((1 << log2ps) < kv.page_size) ++log2ps;
+static void launch_partials_t(const Problem &p, const void *q, const ckv_kv &kv,
+                              const int32_t *idx, int idx_stride, const int32_t *idx_len,
+                              float scale, float *partials, int32_t *err, hipStream_t st) {
     const int ms = attn_max_splits(p, idx_stride);
-    hipLaunchKernelGGL((attn_kernel<T, D, GH>), dim3(ms, p.NG()), dim3(256), 0, st,
+    hipLaunchKernelGGL((attn_kernel<T, D, GH>), dim3(p.NG(), ms), dim3(256), 0, st,
                        static_cast<const T *>(q), static_cast<const T *>(kv.k),
-                       static_cast<const T *>(kv.v), kv.page_table, log2ps, kv.max_pages_per_seq,
-                       kv.num_pages, kv.seq_len, idx, idx_stride, idx_len, p.Hq, p.Hkv, p.gpk,
-                       scale * kLog2e, out, counters, partials, ms, err);
+                       static_cast<const T *>(kv.v), kv.page_table, log2_pow2(kv.page_size),
+                       kv.max_pages_per_seq, kv.num_pages, kv.seq_len, idx, idx_stride, idx_len,
+                       p.Hq, p.Hkv, p.gpk, scale * kLog2e, partials, ms, err);
 }
 
-hipError_t launch_attn(const Problem &p, const void *q, const ckv_kv &kv, const int32_t *idx,
-                       int idx_stride, const int32_t *idx_len, float scale, float *out,
-                       uint32_t *counters, float *partials, int32_t *err, hipStream_t st) {
+hipError_t launch_attn_partials(const Problem &p, const void *q, const ckv_kv &kv,
+                                const int32_t *idx, int idx_stride, const int32_t *idx_len,
+                                float scale, float *partials, int32_t *err, hipStream_t st) {
     const int GH = p.heads_per_graph();
 #define CKV_ATTN_CASE(TT, DT, DD, HH)                                                          \
     if (p.dtype == DT && p.D == DD && GH == HH) {                                              \
-        launch_attn_t<TT, DD, HH>(p, q, kv, idx, idx_stride, idx_len, scale, out, counters,    \
-                                  partials, err, st);                                          \
+        launch_partials_t<TT, DD, HH>(p, q, kv, idx, idx_stride, idx_len, scale, partials,     \
+                                      err, st);                                                \
         return hipGetLastError();                                                              \
     }
     CKV_ATTN_CASE(bf16_t, CKV_DT_BF16, 128, 1) CKV_ATTN_CASE(bf16_t, CKV_DT_BF16, 128, 2)
@@ -288,6 +442,55 @@ hipError_t launch_attn(const Problem &p, const void *q, const ckv_kv &kv, const 
     CKV_ATTN_CASE(float, CKV_DT_F32, 128, 1) CKV_ATTN_CASE(float, CKV_DT_F32, 128, 2)
     CKV_ATTN_CASE(float, CKV_DT_F32, 128, 4) CKV_ATTN_CASE(float, CKV_DT_F32, 128, 8)
 #undef CKV_ATTN_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_merge(const Problem &p, const int32_t *idx_len, int idx_stride, float *out,
+                             const float *partials, hipStream_t st) {
+    const int GH = p.heads_per_graph();
+    const int ms = attn_max_splits(p, idx_stride);
+    const int ch = attn_chunk(p.D, p.elem_bytes());
+#define CKV_MERGE_CASE(DD, HH)                                                                 \
+    if (p.D == DD && GH == HH) {                                                               \
+        hipLaunchKernelGGL((merge_kernel<DD, HH>), dim3(p.NG()), dim3(512),                    \
+                           (size_t)HH * ms * sizeof(float), st, idx_len, idx_stride, ch, p.Hq, \
+                           p.Hkv, p.gpk, out, partials, ms);                                   \
+        return hipGetLastError();                                                              \
+    }
+    CKV_MERGE_CASE(128, 1) CKV_MERGE_CASE(128, 2) CKV_MERGE_CASE(128, 4) CKV_MERGE_CASE(128, 8)
+    CKV_MERGE_CASE(64, 1) CKV_MERGE_CASE(64, 2) CKV_MERGE_CASE(64, 4) CKV_MERGE_CASE(64, 8)
+#undef CKV_MERGE_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge_update(const Problem &p, const int32_t *idx_len, int idx_stride,
+                               float *out, const float *partials, const void *k_new,
+                               const void *v_new, const int32_t *cand, int n_cand,
+                               const ckv_graphs &gr, const ckv_kv &kv, int32_t *assigned,
+                               int32_t *err, hipStream_t st) {
+    const int GH = p.heads_per_graph();
+    const int ms = attn_max_splits(p, idx_stride);
+    const int ch = attn_chunk(p.D, p.elem_bytes());
+    UpdateArgs u{k_new, v_new, cand, n_cand, gr.centroids, gr.num_comms, gr.comm_start,
+                 gr.comm_size, gr.comm_cap, gr.members, p.Cmax, kv.k, kv.v, kv.page_table,
+                 log2_pow2(kv.page_size), kv.max_pages_per_seq, kv.num_pages, kv.seq_len,
+                 assigned, err};
+#define CKV_MU_CASE(TT, DT, DD, HH)                                                            \
+    if (p.dtype == DT && p.D == DD && GH == HH) {                                              \
+        hipLaunchKernelGGL((merge_update_kernel<TT, DD, HH>), dim3(p.NG() + p.B), dim3(512),   \
+                           (size_t)HH * ms * sizeof(float), st, idx_len, idx_stride, ch, p.Hq, \
+                           p.Hkv, p.gpk, p.NG(), out, partials, ms, u);                        \
+        return hipGetLastError();                                                              \
+    }
+    CKV_MU_CASE(bf16_t, CKV_DT_BF16, 128, 1) CKV_MU_CASE(bf16_t, CKV_DT_BF16, 128, 2)
+    CKV_MU_CASE(bf16_t, CKV_DT_BF16, 128, 4) CKV_MU_CASE(bf16_t, CKV_DT_BF16, 128, 8)
+    CKV_MU_CASE(bf16_t, CKV_DT_BF16, 64, 1) CKV_MU_CASE(bf16_t, CKV_DT_BF16, 64, 2)
+    CKV_MU_CASE(bf16_t, CKV_DT_BF16, 64, 4) CKV_MU_CASE(bf16_t, CKV_DT_BF16, 64, 8)
+    CKV_MU_CASE(float, CKV_DT_F32, 128, 1) CKV_MU_CASE(float, CKV_DT_F32, 128, 2)
+    CKV_MU_CASE(float, CKV_DT_F32, 128, 4) CKV_MU_CASE(float, CKV_DT_F32, 128, 8)
+    CKV_MU_CASE(float, CKV_DT_F32, 64, 1) CKV_MU_CASE(float, CKV_DT_F32, 64, 2)
+    CKV_MU_CASE(float, CKV_DT_F32, 64, 4) CKV_MU_CASE(float, CKV_DT_F32, 64, 8)
+#undef CKV_MU_CASE
     return hipErrorInvalidValue;
 }
 

@@ -50,9 +50,11 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Order-preserving map of an fp32 score to u32 (larger score -> larger key).
+// Order-preserving map of an fp32 score to u32 (larger score -> larger key);
+// -0 and +0 compare equal as floats, so both map to the key of +0.
 __device__ __forceinline__ uint32_t order_key(float s) {
     uint32_t u = __float_as_uint(s);
+    if ((u << 1) == 0u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

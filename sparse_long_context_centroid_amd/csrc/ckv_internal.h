@@ -23,7 +23,7 @@ struct Problem {
 // 16-byte-per-lane loads of K and of V; a row of d elements takes d*elem/16 lanes,
 // so one load covers 1024/(d*elem) rows.  Tokens per workgroup:
 constexpr int kAttnWaves = 4;
-constexpr int kAttnLoads = 16;
+constexpr int kAttnLoads = 12;
 constexpr int attn_chunk(int D, int elem_bytes) {
     return kAttnWaves * kAttnLoads * (1024 / (D * elem_bytes));
 }
@@ -32,17 +32,18 @@ inline int attn_max_splits(const Problem &p, int index_stride) {
     return (index_stride + ch - 1) / ch;
 }
 
-// Workspace of ckv_sparse_decode_attn: [counters: NG u32, padded to 256 B]
-// [partials: NG * GH * max_splits * (D + 2) fp32].
-inline size_t attn_counter_bytes(const Problem &p) {
-    return ((size_t)p.NG() * 4 + 255) / 256 * 256;
+inline int log2_pow2(int x) {
+    int l = 0;
+    while ((1 << l) < x) ++l;
+    return l;
 }
+
+// Workspace of the attention call: partials NG * GH * max_splits * (D + 2) fp32.
 inline size_t attn_partial_floats(const Problem &p, int index_stride) {
     return (size_t)p.NG() * p.heads_per_graph() * attn_max_splits(p, index_stride) * (p.D + 2);
 }
 
-hipError_t launch_stage_query(const Problem &p, const void *q, double *q64, hipStream_t st);
-hipError_t launch_score(const Problem &p, const double *q64, const ckv_graphs &gr, double scale,
+hipError_t launch_score(const Problem &p, const void *q, const ckv_graphs &gr, double scale,
                         float *scores, hipStream_t st);
 hipError_t launch_rows_to_interleaved(const Problem &p, const float *rows, float *cent,
                                       hipStream_t st);
@@ -52,12 +53,18 @@ hipError_t launch_select(const Problem &p, const float *scores, const ckv_graphs
                          const int32_t *budget, const int32_t *seq_len, int n_cand,
                          int32_t *idx, int idx_stride, int32_t *idx_len, int32_t *num_sel,
                          int32_t *cand, uint8_t *selected, int32_t *err, hipStream_t st);
-hipError_t launch_attn(const Problem &p, const void *q, const ckv_kv &kv, const int32_t *idx,
-                       int idx_stride, const int32_t *idx_len, float scale, float *out,
-                       uint32_t *counters, float *partials, int32_t *err, hipStream_t st);
+hipError_t launch_attn_partials(const Problem &p, const void *q, const ckv_kv &kv,
+                                const int32_t *idx, int idx_stride, const int32_t *idx_len,
+                                float scale, float *partials, int32_t *err, hipStream_t st);
+hipError_t launch_attn_merge(const Problem &p, const int32_t *idx_len, int idx_stride, float *out,
+                             const float *partials, hipStream_t st);
+hipError_t launch_merge_update(const Problem &p, const int32_t *idx_len, int idx_stride,
+                               float *out, const float *partials, const void *k_new,
+                               const void *v_new, const int32_t *cand, int n_cand,
+                               const ckv_graphs &gr, const ckv_kv &kv, int32_t *assigned,
+                               int32_t *err, hipStream_t st);
 hipError_t launch_update(const Problem &p, const void *k_new, const void *v_new,
                          const int32_t *cand, int n_cand, const ckv_graphs &gr, const ckv_kv &kv,
                          int32_t *assigned, int32_t *err, hipStream_t st);
-hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t st);
 
 }  // namespace ckv

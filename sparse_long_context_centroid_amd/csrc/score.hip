@@ -17,47 +17,41 @@
 
 namespace ckv {
 
-// q [B][Hq][d] (T) -> q64 [NG][d/4][GH][4] fp64; GH = heads per graph.
-template <typename T>
-__global__ __launch_bounds__(256) void stage_query_kernel(const T *__restrict__ q,
-                                                          double *__restrict__ q64, int Hq,
-                                                          int Hkv, int gpk, int D, int GH) {
-    const int g = blockIdx.x;
+constexpr int kScoreThreads = 256;
+
+// One workgroup = 256 consecutive communities of one graph, one per lane.  The
+// graph's GH query rows are widened to fp64 once into LDS, laid out [d/4][GH][4]
+// so that each step's 4*GH values are one contiguous broadcast read.
+template <typename T, int D, int GH>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(
+    const T *__restrict__ q, const float *__restrict__ cent, const int32_t *__restrict__ num_comms,
+    const int32_t *__restrict__ comm_size, int Cmax, int Hq, int Hkv, int gpk, double scale,
+    float *__restrict__ scores) {
+    __shared__ double sq[D * GH];
+    const int g = blockIdx.y;
+    const int C = min(num_comms[g], Cmax);
+    const int base = blockIdx.x * kScoreThreads;
+    if (base >= C) return;
+    const int c = base + threadIdx.x;
+    const bool live = c < C;
     const int G = Hq / Hkv;
     const int b = g / (Hkv * gpk);
     const int kvh = (g / gpk) % Hkv;
-    const int j = g % gpk;
-    const int h0 = kvh * G + (gpk == 1 ? 0 : j);
-    const int total = GH * D;
-    for (int t = threadIdx.x; t < total; t += blockDim.x) {
-        // destination order: k = i/4, h, e = i%4
-        const int k = t / (GH * 4);
-        const int h = (t / 4) % GH;
-        const int e = t % 4;
-        const int i = k * 4 + e;
-        q64[(size_t)g * total + t] = (double)to_f32(q[((size_t)b * Hq + h0 + h) * D + i]);
+    const int h0 = kvh * G + (gpk == 1 ? 0 : g % gpk);
+    // Stage the graph's queries in LDS before the centroid stream starts: a query
+    // load issued behind 32 KiB of centroid requests per wave would wait for the
+    // whole stream.
+    for (int t = threadIdx.x; t < D * GH; t += kScoreThreads) {
+        const int k = t / (GH * 4), h = (t / 4) % GH, e = t % 4;
+        sq[t] = (double)to_f32(q[((size_t)b * Hq + h0 + h) * D + k * 4 + e]);
     }
-}
-
-template <int D, int GH>
-__global__ __launch_bounds__(64) void score_kernel(const double *__restrict__ q64,
-                                                   const float *__restrict__ cent,
-                                                   const int32_t *__restrict__ num_comms,
-                                                   const int32_t *__restrict__ comm_size,
-                                                   int Cmax, double scale,
-                                                   float *__restrict__ scores) {
-    const int g = blockIdx.y;
-    const int C = min(num_comms[g], Cmax);
-    const int c = blockIdx.x * kWave + threadIdx.x;
-    if (blockIdx.x * kWave >= C) return;
-    const bool live = c < C;
-    const int cc = live ? c : 0;
-    const float4 *cp = reinterpret_cast<const float4 *>(cent) + (size_t)g * (D / 4) * Cmax + cc;
-    const double *qg = q64 + (size_t)g * (D / 4) * GH * 4;
-
+    __syncthreads();
+    const float4 *cp = reinterpret_cast<const float4 *>(cent) + (size_t)g * (D / 4) * Cmax +
+                       (live ? c : base);
     float4 v[D / 4];
 #pragma unroll
     for (int k = 0; k < D / 4; ++k) v[k] = cp[(size_t)k * Cmax];
+    const int sz = live ? comm_size[(size_t)g * Cmax + c] : 0;
 
     double acc[GH];
 #pragma unroll
@@ -67,7 +61,7 @@ __global__ __launch_bounds__(64) void score_kernel(const double *__restrict__ q6
         const double e0 = v[k].x, e1 = v[k].y, e2 = v[k].z, e3 = v[k].w;
 #pragma unroll
         for (int h = 0; h < GH; ++h) {
-            const double *qq = qg + (k * GH + h) * 4;
+            const double *qq = sq + (k * GH + h) * 4;
             acc[h] = fma(qq[0], e0, acc[h]);
             acc[h] = fma(qq[1], e1, acc[h]);
             acc[h] = fma(qq[2], e2, acc[h]);
@@ -78,10 +72,7 @@ __global__ __launch_bounds__(64) void score_kernel(const double *__restrict__ q6
 #pragma unroll
     for (int h = 1; h < GH; ++h)
         if (acc[h] > best) best = acc[h];
-    if (live) {
-        const int sz = comm_size[(size_t)g * Cmax + c];
-        scores[(size_t)g * Cmax + c] = sz > 0 ? (float)(best * scale) : -__builtin_inff();
-    }
+    if (live) scores[(size_t)g * Cmax + c] = sz > 0 ? (float)(best * scale) : -__builtin_inff();
 }
 
 // ---- layout helpers ---------------------------------------------------------------
@@ -110,31 +101,31 @@ __global__ void interleaved_to_rows_kernel(const float *__restrict__ cent, float
 }
 
 // ---- launchers ----------------------------------------------------------------------
-hipError_t launch_stage_query(const Problem &p, const void *q, double *q64, hipStream_t st) {
-    const int GH = p.heads_per_graph();
-    if (p.dtype == CKV_DT_BF16)
-        hipLaunchKernelGGL(stage_query_kernel<bf16_t>, dim3(p.NG()), dim3(256), 0, st,
-                           static_cast<const bf16_t *>(q), q64, p.Hq, p.Hkv, p.gpk, p.D, GH);
-    else
-        hipLaunchKernelGGL(stage_query_kernel<float>, dim3(p.NG()), dim3(256), 0, st,
-                           static_cast<const float *>(q), q64, p.Hq, p.Hkv, p.gpk, p.D, GH);
-    return hipGetLastError();
+template <typename T, int D, int GH>
+static void launch_score_t(const Problem &p, const void *q, const ckv_graphs &gr, double scale,
+                           float *scores, hipStream_t st) {
+    hipLaunchKernelGGL((score_kernel<T, D, GH>),
+                       dim3((p.Cmax + kScoreThreads - 1) / kScoreThreads, p.NG()),
+                       dim3(kScoreThreads), 0, st, static_cast<const T *>(q), gr.centroids,
+                       gr.num_comms, gr.comm_size, p.Cmax, p.Hq, p.Hkv, p.gpk, scale, scores);
 }
 
-template <int D, int GH>
-static void launch_score_t(const Problem &p, const double *q64, const ckv_graphs &gr,
-                           double scale, float *scores, hipStream_t st) {
-    hipLaunchKernelGGL((score_kernel<D, GH>), dim3(p.Cmax / kWave, p.NG()), dim3(kWave), 0, st,
-                       q64, gr.centroids, gr.num_comms, gr.comm_size, p.Cmax, scale, scores);
-}
-
-hipError_t launch_score(const Problem &p, const double *q64, const ckv_graphs &gr, double scale,
+hipError_t launch_score(const Problem &p, const void *q, const ckv_graphs &gr, double scale,
                         float *scores, hipStream_t st) {
     const int GH = p.heads_per_graph();
-#define CKV_SCORE_CASE(DD, HH) \
-    if (p.D == DD && GH == HH) { launch_score_t<DD, HH>(p, q64, gr, scale, scores, st); return hipGetLastError(); }
-    CKV_SCORE_CASE(64, 1) CKV_SCORE_CASE(64, 2) CKV_SCORE_CASE(64, 4) CKV_SCORE_CASE(64, 8)
-    CKV_SCORE_CASE(128, 1) CKV_SCORE_CASE(128, 2) CKV_SCORE_CASE(128, 4) CKV_SCORE_CASE(128, 8)
+#define CKV_SCORE_CASE(TT, DT, DD, HH)                                                         \
+    if (p.dtype == DT && p.D == DD && GH == HH) {                                              \
+        launch_score_t<TT, DD, HH>(p, q, gr, scale, scores, st);                               \
+        return hipGetLastError();                                                              \
+    }
+    CKV_SCORE_CASE(bf16_t, CKV_DT_BF16, 128, 1) CKV_SCORE_CASE(bf16_t, CKV_DT_BF16, 128, 2)
+    CKV_SCORE_CASE(bf16_t, CKV_DT_BF16, 128, 4) CKV_SCORE_CASE(bf16_t, CKV_DT_BF16, 128, 8)
+    CKV_SCORE_CASE(bf16_t, CKV_DT_BF16, 64, 1) CKV_SCORE_CASE(bf16_t, CKV_DT_BF16, 64, 2)
+    CKV_SCORE_CASE(bf16_t, CKV_DT_BF16, 64, 4) CKV_SCORE_CASE(bf16_t, CKV_DT_BF16, 64, 8)
+    CKV_SCORE_CASE(float, CKV_DT_F32, 128, 1) CKV_SCORE_CASE(float, CKV_DT_F32, 128, 2)
+    CKV_SCORE_CASE(float, CKV_DT_F32, 128, 4) CKV_SCORE_CASE(float, CKV_DT_F32, 128, 8)
+    CKV_SCORE_CASE(float, CKV_DT_F32, 64, 1) CKV_SCORE_CASE(float, CKV_DT_F32, 64, 2)
+    CKV_SCORE_CASE(float, CKV_DT_F32, 64, 4) CKV_SCORE_CASE(float, CKV_DT_F32, 64, 8)
 #undef CKV_SCORE_CASE
     return hipErrorInvalidValue;
 }

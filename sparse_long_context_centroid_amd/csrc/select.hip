@@ -8,40 +8,166 @@
 //   cand   : the first n_cand communities of the same order (update candidates)
 //   list   : 0..min(S,n)-1, then members of kept communities in ascending id.
 //
-// One 1024-thread workgroup per graph; everything lives in LDS / registers.
-// The prefix is found without sorting: a most-significant-digit-first radix
-// select over order-preserving u32 score keys (4 passes of 8 bits) whose
-// histograms are weighted by community size (the kept prefix) and by 1 (the
-// candidates) at the same time; a wavefront suffix scan over each 256-bin
-// histogram finds the digit where the running weight crosses the remaining
-// budget.  Communities still tied on the full 32-bit key after 4 passes are
-// resolved by an id-ordered prefix sum, which is exactly the (score desc, id asc)
-// order restricted to the tie.  Thread t holds communities t*IPT .. t*IPT+IPT-1,
-// so the block scans are in id order.
+// One 512-thread workgroup per graph; thread t holds communities t*IPT ..
+// t*IPT+IPT-1 in registers, so every block scan runs in id order.
+//
+// The kept prefix is found without sorting.  Fast path: the scores are binned
+// into 256 buckets linear in the score between the graph's min and max (a
+// monotone map, so each bucket is a contiguous stretch of the order); one
+// size-weighted histogram (and one unit-weighted for the candidates) gives the
+// crossing bucket; buckets above it are kept, below dropped, and the communities
+// inside it (a handful) are ranked exactly by one wavefront.  General path, when
+// the crossing bucket holds more than 64 communities (e.g. many equal scores):
+// with u32 keys that preserve the fp32 score order, the prefix is {key > T*} plus
+// an id-ordered prefix of {key == T*}, where T* is the smallest key with
+// W(key > T*) <= budget (W = sum of sizes); W(key > T) does not increase with T,
+// so T* is found by a 4-ary search on the key, one size-weighted block reduction
+// per probe.  Both paths give exactly the (score desc, id asc) prefix.  The member lists of the kept communities are then
+// copied with one flat, balanced pass (each thread finds its community by binary
+// search over the compacted offsets), so all member loads are in flight at once.
 #include "ckv_device.h"
 #include "ckv_internal.h"
 
 namespace ckv {
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / kWave;
 
-enum : uint8_t { ST_REJ = 0, ST_PEND = 1, ST_SEL = 2 };
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int x) {
+    // lanes whose source is outside the row (or whose row is masked off) read 0
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, true);
+}
 
-// Inclusive wave scan (sum) of an int.
+// Inclusive wavefront scan (sum) of an int with DPP only: Hillis-Steele inside each
+// row of 16 lanes (row_shr 1, 2, 4, 8), then row_bcast 15 / 31 carry the row
+// totals into the following rows.
 __device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    x += dpp_i<0x111>(x);        // row_shr:1
+    x += dpp_i<0x112>(x);        // row_shr:2
+    x += dpp_i<0x114>(x);        // row_shr:4
+    x += dpp_i<0x118>(x);        // row_shr:8
+    x += dpp_i<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_i<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
     return x;
 }
 
-// Exclusive block scan of two ints at once; returns the exclusive prefixes and
-// the block totals.  `tmp` holds 2*kSelWaves ints.  Ends with a barrier, so the
-// caller may reuse `tmp` only after another barrier.
+// Sum of an int over the wavefront, as a wave-uniform value.
+__device__ __forceinline__ int wave_sum(int x) {
+    return __builtin_amdgcn_readlane(wave_incl_scan(x), kWave - 1);
+}
+
+// Block sums of N ints (all threads get all N); `buf` holds N*kSelWaves ints and
+// must not be written again before the next barrier.
+template <int N>
+__device__ __forceinline__ void block_sums(int (&v)[N], int *buf) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = wave_sum(v[j]);
+    if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) buf[j * kSelWaves + w] = v[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        int t = 0;
+#pragma unroll
+        for (int i = 0; i < kSelWaves; ++i) t += buf[j * kSelWaves + i];
+        v[j] = t;
+    }
+}
+
+// Block maxima of two floats (all threads get both); `buf` holds 2*kSelWaves.
+__device__ __forceinline__ void block_max2(float (&v)[2], float *buf) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) v[j] = fmaxf(v[j], __shfl_xor(v[j], off));
+    }
+    if (lane == 0) {
+        buf[w] = v[0];
+        buf[kSelWaves + w] = v[1];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float t = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < kSelWaves; ++i) t = fmaxf(t, buf[j * kSelWaves + i]);
+        v[j] = t;
+    }
+}
+
+// One wavefront: given a 256-bin histogram, find the bin where the weight summed
+// from the top first exceeds `cap`.  out[0] = that bin (-1 when the whole
+// histogram fits), out[1] = weight of the bins above it.
+__device__ __forceinline__ void find_crossing(const int *hist, int cap, int *out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int h[4];
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[i] = hist[lane * 4 + i];
+        t += h[i];
+    }
+    int s = t;  // suffix over lanes: sum over lanes >= this one
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_down(s, off);
+        if (lane + off < kWave) s += y;
+    }
+    const int total = __shfl(s, 0);
+    if (total <= cap) {
+        if (lane == 0) {
+            out[0] = -1;
+            out[1] = total;
+        }
+        return;
+    }
+    int above = s - t;
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+        const int incl = above + h[i];
+        if (above <= cap && incl > cap) {
+            out[0] = lane * 4 + i;
+            out[1] = above;
+        }
+        above = incl;
+    }
+}
+
+// Communities inside the crossing bucket that the fast path ranks exactly.
+constexpr int kPend = 64;
+
+// One round of the 4-ary search for the smallest T in [lo, hi] with f(T) <= cap,
+// f non-increasing; f1..f3 are f at the three probe points t1 < t2 < t3.
+__device__ __forceinline__ void narrow(uint32_t &lo, uint32_t &hi, const uint32_t (&t)[3],
+                                       const int (&f)[3], int cap) {
+    if (f[0] <= cap) {
+        hi = t[0];
+    } else if (f[1] <= cap) {
+        lo = t[0] + 1;
+        hi = t[1];
+    } else if (f[2] <= cap) {
+        lo = t[1] + 1;
+        hi = t[2];
+    } else {
+        lo = t[2] + 1;
+    }
+}
+
+__device__ __forceinline__ void probes(uint32_t lo, uint32_t hi, uint32_t (&t)[3]) {
+    const uint64_t wdt = (uint64_t)hi - lo;
+    t[0] = lo + (uint32_t)(wdt / 4);
+    t[1] = lo + (uint32_t)(wdt / 2);
+    t[2] = lo + (uint32_t)(wdt * 3 / 4);
+}
+
+// Exclusive block scan of two ints; also returns the totals.  Ends with a barrier.
 __device__ __forceinline__ void block_excl_scan2(int a, int b, int &ea, int &eb, int &ta, int &tb,
                                                  int *tmp) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -71,63 +197,28 @@ __device__ __forceinline__ void block_excl_scan2(int a, int b, int &ea, int &eb,
     __syncthreads();
 }
 
-// Wave 0: given a 256-bin histogram, find the crossing digit.
-//   out[0] = digit (or -1 when the whole histogram fits in `rem`)
-//   out[1] = weight of the bins above that digit
-__device__ __forceinline__ void find_crossing(const int *hist, int rem, int *out) {
-    const int lane = threadIdx.x;  // wave 0 only
-    int h[4];
-    int t = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        h[i] = hist[lane * 4 + i];
-        t += h[i];
-    }
-    // suffix over lanes: S_l = sum_{l' >= l} t_l'
-    int s = t;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_down(s, off);
-        if (lane + off < kWave) s += y;
-    }
-    const int total = __shfl(s, 0);
-    if (total <= rem) {
-        if (lane == 0) {
-            out[0] = -1;
-            out[1] = total;
-        }
-        return;
-    }
-    int above = s - t;  // weight of the bins of higher lanes
-#pragma unroll
-    for (int i = 3; i >= 0; --i) {
-        const int incl = above + h[i];
-        if (above <= rem && incl > rem) {
-            out[0] = lane * 4 + i;
-            out[1] = above;
-        }
-        above = incl;
-    }
-}
-
 template <int IPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ num_comms,
-    const int32_t *__restrict__ comm_start, const int32_t *__restrict__ comm_size,
-    const int32_t *__restrict__ members, int Cmax, int graphs_per_seq,
+    const int32_t *__restrict__ comm_start, int32_t *__restrict__ comm_size,
+    int32_t *__restrict__ members, int Cmax, int graphs_per_seq,
     const int32_t *__restrict__ budget, const int32_t *__restrict__ seq_len, int S, int M,
     int32_t *__restrict__ idx, int idx_stride, int32_t *__restrict__ idx_len,
     int32_t *__restrict__ num_sel, int32_t *__restrict__ cand, uint8_t *__restrict__ selected,
     int32_t *__restrict__ err) {
-    __shared__ int histA[256];
-    __shared__ int histB[256];
-    __shared__ int cross[4];
+    __shared__ int red[2][6 * kSelWaves];
     __shared__ int scan_tmp[2 * kSelWaves];
     __shared__ int list_start[CKV_MAX_COMMS];
     __shared__ int list_off[CKV_MAX_COMMS + 1];
     __shared__ uint32_t cand_key[CKV_MAX_CAND];
     __shared__ int cand_id[CKV_MAX_CAND];
     __shared__ int cand_n;
+    __shared__ int histA[256], histB[256], cross[4];
+    __shared__ float fred[2 * kSelWaves];
+    __shared__ uint32_t pendA_key[kPend], pendB_key[kPend];
+    __shared__ int pendA_id[kPend], pendB_id[kPend], pendA_w[kPend];
+    __shared__ bool pendA_sel[kPend], pendB_sel[kPend];
+    __shared__ int pendA_n, pendB_n;
 
     const int g = blockIdx.x;
     const int tid = threadIdx.x;
@@ -136,95 +227,192 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int b = g / graphs_per_seq;
     const int C = min(num_comms[g], Cmax);
     const int n = seq_len[b];
-    int remA = budget[b] < 0 ? 0 : budget[b];
-    int remB = M;
+    const int Bt = budget[b] < 0 ? 0 : budget[b];
 
+    // sizes, scores and member offsets of this thread's communities, all in flight
     uint32_t key[IPT];
-    int wt[IPT];
-    uint8_t stA[IPT], stB[IPT];
+    float sc[IPT];
+    int wt[IPT], cst[IPT];
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
         const int c = tid * IPT + i;
-        const bool v = c < C && comm_size[(size_t)g * Cmax + c] > 0;
-        wt[i] = v ? comm_size[(size_t)g * Cmax + c] : 0;
-        key[i] = v ? order_key(scores[(size_t)g * Cmax + c]) : 0u;
-        stA[i] = v ? ST_PEND : ST_REJ;
-        stB[i] = v ? ST_PEND : ST_REJ;
+        const size_t o = (size_t)g * Cmax + (c < C ? c : 0);
+        wt[i] = c < C ? comm_size[o] : 0;
+        sc[i] = c < C ? scores[o] : 0.f;
+        cst[i] = c < C ? comm_start[o] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        // valid keys are >= 1; 0 marks an empty or unused community
+        key[i] = wt[i] > 0 ? max(order_key(sc[i]), 1u) : 0u;
+        wt[i] = wt[i] > 0 ? wt[i] : 0;
     }
     if (tid == 0) cand_n = 0;
 
-    bool doneA = false, doneB = false;
-    for (int pass = 0; pass < 4 && !(doneA && doneB); ++pass) {
-        const int shift = 24 - 8 * pass;
-        if (tid < 256) {
-            histA[tid] = 0;
-            histB[tid] = 0;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < IPT; ++i) {
-            const int dg = (key[i] >> shift) & 255;
-            if (stA[i] == ST_PEND) atomicAdd(&histA[dg], wt[i]);
-            if (stB[i] == ST_PEND) atomicAdd(&histB[dg], 1);
-        }
-        __syncthreads();
-        if (w == 0) {
-            if (!doneA) find_crossing(histA, remA, cross);
-            if (!doneB) find_crossing(histB, remB, cross + 2);
-        }
-        __syncthreads();
-        if (!doneA) {
-            const int dA = cross[0];
-#pragma unroll
-            for (int i = 0; i < IPT; ++i) {
-                if (stA[i] != ST_PEND) continue;
-                const int dg = (key[i] >> shift) & 255;
-                stA[i] = (dA < 0 || dg > dA) ? ST_SEL : (dg < dA ? ST_REJ : ST_PEND);
-            }
-            remA -= cross[1];
-            doneA = dA < 0;
-        }
-        if (!doneB) {
-            const int dB = cross[2];
-#pragma unroll
-            for (int i = 0; i < IPT; ++i) {
-                if (stB[i] != ST_PEND) continue;
-                const int dg = (key[i] >> shift) & 255;
-                stB[i] = (dB < 0 || dg > dB) ? ST_SEL : (dg < dB ? ST_REJ : ST_PEND);
-            }
-            remB -= cross[3];
-            doneB = dB < 0;
-        }
-        __syncthreads();
-    }
-
-    // Ties on the full key: keep the id-ordered prefix that fits.
-    {
-        int la = 0, lb = 0;
-#pragma unroll
-        for (int i = 0; i < IPT; ++i) {
-            la += stA[i] == ST_PEND ? wt[i] : 0;
-            lb += stB[i] == ST_PEND ? 1 : 0;
-        }
-        int ea, eb, ta, tb;
-        block_excl_scan2(la, lb, ea, eb, ta, tb, scan_tmp);
-#pragma unroll
-        for (int i = 0; i < IPT; ++i) {
-            if (stA[i] == ST_PEND) {
-                stA[i] = (ea + wt[i] <= remA) ? ST_SEL : ST_REJ;
-                ea += wt[i];
-            }
-            if (stB[i] == ST_PEND) {
-                stB[i] = (eb + 1 <= remB) ? ST_SEL : ST_REJ;
-                eb += 1;
-            }
-        }
-    }
-
-    // Candidates: at most M, gathered then ordered by (key desc, id asc).
+    // ---- fast path: one size-weighted histogram over 256 score buckets that are
+    // linear in the fp32 score (monotone, so every bucket is a contiguous range of
+    // the order); everything above the crossing bucket is kept, everything below
+    // dropped, and the few communities inside it are ranked exactly by one wave.
+    bool selA[IPT], selB[IPT];
+    float lo_s = __builtin_inff(), hi_s = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-        if (stB[i] == ST_SEL) {
+        if (wt[i] > 0) {
+            lo_s = fminf(lo_s, sc[i]);
+            hi_s = fmaxf(hi_s, sc[i]);
+        }
+    }
+    {
+        float v2[2] = {-lo_s, hi_s};
+        block_max2(v2, fred);
+        lo_s = -v2[0];
+        hi_s = v2[1];
+    }
+    const bool spread = hi_s > lo_s && hi_s - lo_s < __builtin_inff();
+    const float bscale = spread ? 255.99f / (hi_s - lo_s) : 0.f;
+    int bk[IPT];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const float x = (sc[i] - lo_s) * bscale;
+        bk[i] = wt[i] > 0 ? min(255, max(0, (int)x)) : -1;
+    }
+    for (int t = tid; t < 256; t += kSelThreads) {
+        histA[t] = 0;
+        histB[t] = 0;
+    }
+    if (tid == 0) {
+        pendA_n = 0;
+        pendB_n = 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        if (bk[i] >= 0) {
+            atomicAdd(&histA[bk[i]], wt[i]);
+            atomicAdd(&histB[bk[i]], 1);
+        }
+    }
+    __syncthreads();
+    if (w == 0) find_crossing(histA, Bt, cross);
+    if (w == 1) find_crossing(histB, M, cross + 2);
+    __syncthreads();
+    const int bA = cross[0], aboveA_b = cross[1], bB = cross[2], aboveB_b = cross[3];
+    int slotA[IPT], slotB[IPT];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        slotA[i] = -1;
+        slotB[i] = -1;
+        selA[i] = bk[i] >= 0 && (bA < 0 || bk[i] > bA);
+        selB[i] = bk[i] >= 0 && (bB < 0 || bk[i] > bB);
+        if (bk[i] >= 0 && bk[i] == bA) {
+            slotA[i] = atomicAdd(&pendA_n, 1);
+            if (slotA[i] < kPend) {
+                pendA_key[slotA[i]] = key[i];
+                pendA_id[slotA[i]] = tid * IPT + i;
+                pendA_w[slotA[i]] = wt[i];
+            }
+        }
+        if (bk[i] >= 0 && bk[i] == bB) {
+            slotB[i] = atomicAdd(&pendB_n, 1);
+            if (slotB[i] < kPend) {
+                pendB_key[slotB[i]] = key[i];
+                pendB_id[slotB[i]] = tid * IPT + i;
+            }
+        }
+    }
+    __syncthreads();
+    const int nPA = pendA_n, nPB = pendB_n;
+    if (nPA <= kPend && nPB <= kPend) {
+        // exact rank of each pending community among the pending ones, in the
+        // (score desc, id asc) order: kept iff everything before it still fits
+        if (w == 0 && lane < nPA) {
+            const uint32_t k0 = pendA_key[lane];
+            const int i0 = pendA_id[lane];
+            int before = 0;
+            for (int j = 0; j < nPA; ++j) {
+                const uint32_t kj = pendA_key[j];
+                if (kj > k0 || (kj == k0 && pendA_id[j] < i0)) before += pendA_w[j];
+            }
+            pendA_sel[lane] = aboveA_b + before + pendA_w[lane] <= Bt;
+        }
+        if (w == 1 && lane < nPB) {
+            const uint32_t k0 = pendB_key[lane];
+            const int i0 = pendB_id[lane];
+            int before = 0;
+            for (int j = 0; j < nPB; ++j) {
+                const uint32_t kj = pendB_key[j];
+                if (kj > k0 || (kj == k0 && pendB_id[j] < i0)) before += 1;
+            }
+            pendB_sel[lane] = aboveB_b + before + 1 <= M;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+            if (slotA[i] >= 0) selA[i] = pendA_sel[slotA[i]];
+            if (slotB[i] >= 0) selB[i] = pendB_sel[slotB[i]];
+        }
+    } else {
+        // ---- general path (e.g. many equal scores): exact 4-ary search on the keys
+        // for the smallest T with W(key > T) <= Bt (A, size weights) and the
+        // smallest U with N(key > U) <= M (B, unit weights); W(key > 0xFFFFFFFF) = 0,
+        // so the answer always lies in [lo, hi].  Ties at T / U are resolved by
+        // an id-ordered prefix sum.
+        uint32_t loA = 0, hiA = 0xFFFFFFFFu, loB = 0, hiB = 0xFFFFFFFFu;
+        for (int it = 0; (loA != hiA || loB != hiB) && it < 40; ++it) {
+            uint32_t tA[3], tB[3];
+            probes(loA, hiA, tA);
+            probes(loB, hiB, tB);
+            int v[6] = {0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < IPT; ++i) {
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    v[j] += key[i] > tA[j] ? wt[i] : 0;
+                    v[3 + j] += key[i] > tB[j] ? 1 : 0;
+                }
+            }
+            block_sums<6>(v, red[it & 1]);
+            const int fA[3] = {v[0], v[1], v[2]}, fB[3] = {v[3], v[4], v[5]};
+            if (loA != hiA) narrow(loA, hiA, tA, fA, Bt);
+            if (loB != hiB) narrow(loB, hiB, tB, fB, M);
+        }
+        const uint32_t TA = loA, TB = loB;
+        int aboveA = 0, aboveB = 0, tieA = 0, tieB = 0;
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+            aboveA += key[i] > TA ? wt[i] : 0;
+            aboveB += key[i] > TB ? 1 : 0;
+            tieA += (key[i] == TA && TA > 0) ? wt[i] : 0;
+            tieB += (key[i] == TB && TB > 0) ? 1 : 0;
+        }
+        int exA, exB, totTieA, totTieB;
+        block_excl_scan2(tieA, tieB, exA, exB, totTieA, totTieB, scan_tmp);
+        int remA, remB;
+        {
+            int v[2] = {aboveA, aboveB};
+            block_sums<2>(v, red[0]);
+            remA = Bt - v[0];
+            remB = M - v[1];
+        }
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+            bool sa = key[i] > TA;
+            bool sb = key[i] > TB;
+            if (key[i] == TA && TA > 0) {
+                sa = exA + wt[i] <= remA;
+                exA += wt[i];
+            }
+            if (key[i] == TB && TB > 0) {
+                sb = exB + 1 <= remB;
+                exB += 1;
+            }
+            selA[i] = sa && wt[i] > 0;
+            selB[i] = sb && wt[i] > 0;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        if (selB[i]) {
             const int slot = atomicAdd(&cand_n, 1);
             if (slot < CKV_MAX_CAND) {
                 cand_key[slot] = key[i];
@@ -233,53 +421,29 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
     }
 
-    // Compaction offsets in id order.
+    // compaction offsets in id order
     int la = 0, lc = 0;
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-        la += stA[i] == ST_SEL ? wt[i] : 0;
-        lc += stA[i] == ST_SEL ? 1 : 0;
+        la += selA[i] ? wt[i] : 0;
+        lc += selA[i] ? 1 : 0;
     }
     int ea, ec, total, ksel;
     block_excl_scan2(la, lc, ea, ec, total, ksel, scan_tmp);
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
         const int c = tid * IPT + i;
-        if (stA[i] == ST_SEL) {
-            list_start[ec] = comm_start[(size_t)g * Cmax + c];
+        if (selA[i]) {
+            list_start[ec] = cst[i];
             list_off[ec] = ea;
             ea += wt[i];
             ec += 1;
         }
-        if (selected && c < Cmax) selected[(size_t)g * Cmax + c] = stA[i] == ST_SEL ? 1 : 0;
+        if (selected && c < Cmax) selected[(size_t)g * Cmax + c] = selA[i] ? 1 : 0;
     }
-    if (tid == 0) list_off[ksel] = total;
-    __syncthreads();
-
-    const int ns = S < n ? S : n;
-    int32_t *out = idx + (size_t)g * idx_stride;
-    bool overflow = false;
-    for (int t = tid; t < ns; t += kSelThreads) {
-        if (t < idx_stride) out[t] = t;
-        else overflow = true;
-    }
-    for (int e = w; e < ksel; e += kSelWaves) {
-        const int st = list_start[e];
-        const int o0 = ns + list_off[e];
-        const int sz = list_off[e + 1] - list_off[e];
-        for (int j = lane; j < sz; j += kWave) {
-            const int o = o0 + j;
-            if (o < idx_stride) out[o] = members[(size_t)st + j];
-            else overflow = true;
-        }
-    }
-    if (overflow) set_err(err, CKV_DEVERR_INDEX_RANGE);
-
     if (tid == 0) {
-        const int len = ns + total;
-        idx_len[g] = len < idx_stride ? len : idx_stride;
-        if (num_sel) num_sel[g] = ksel;
-        // order the candidates (at most CKV_MAX_CAND) by (key desc, id asc)
+        list_off[ksel] = total;
+        // order the candidates (at most M <= CKV_MAX_CAND) by (key desc, id asc)
         const int nc = cand_n < M ? cand_n : M;
         for (int a = 1; a < nc; ++a) {
             const uint32_t kk = cand_key[a];
@@ -293,8 +457,55 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             cand_key[p + 1] = kk;
             cand_id[p + 1] = ii;
         }
-        for (int a = 0; a < M; ++a) cand[(size_t)g * M + a] = a < nc ? cand_id[a] : -1;
+        for (int a = nc; a < M; ++a) cand_id[a] = -1;
     }
+    __syncthreads();
+
+    const int ns = S < n ? S : n;
+    int32_t *out = idx + (size_t)g * idx_stride;
+    bool overflow = false;
+    for (int t = tid; t < ns; t += kSelThreads) {
+        if (t < idx_stride) out[t] = t;
+        else overflow = true;
+    }
+    // flat copy of the kept member lists: output slot p (0 <= p < total) belongs
+    // to the compacted community e with list_off[e] <= p < list_off[e+1]
+    constexpr int kBatch = 8;
+    for (int p0 = 0; p0 < total; p0 += kBatch * kSelThreads) {
+        int src[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int p = p0 + k * kSelThreads + tid;
+            src[k] = -1;
+            if (p < total) {
+                int lo = 0, hi = ksel - 1;  // last e with list_off[e] <= p
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (list_off[mid] <= p) lo = mid; else hi = mid - 1;
+                }
+                src[k] = list_start[lo] + (p - list_off[lo]);
+            }
+        }
+        int val[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) val[k] = src[k] >= 0 ? members[(size_t)src[k]] : 0;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int o = ns + p0 + k * kSelThreads + tid;
+            if (src[k] >= 0) {
+                if (o < idx_stride) out[o] = val[k];
+                else overflow = true;
+            }
+        }
+    }
+    if (overflow) set_err(err, CKV_DEVERR_INDEX_RANGE);
+    if (tid < M) cand[(size_t)g * M + tid] = cand_id[tid];
+    if (tid == 0) {
+        const int len = ns + total;
+        idx_len[g] = len < idx_stride ? len : idx_stride;
+        if (num_sel) num_sel[g] = ksel;
+    }
+
 }
 
 hipError_t launch_select(const Problem &p, const float *scores, const ckv_graphs &gr,
@@ -302,15 +513,16 @@ hipError_t launch_select(const Problem &p, const float *scores, const ckv_graphs
                          int32_t *idx, int idx_stride, int32_t *idx_len, int32_t *num_sel,
                          int32_t *cand, uint8_t *selected, int32_t *err, hipStream_t st) {
     const int ipt = (p.Cmax + kSelThreads - 1) / kSelThreads;
-#define CKV_SEL_CASE(I)                                                                        \
-    if (ipt <= I) {                                                                            \
-        hipLaunchKernelGGL(select_kernel<I>, dim3(p.NG()), dim3(kSelThreads), 0, st, scores,   \
-                           gr.num_comms, gr.comm_start, gr.comm_size, gr.members, p.Cmax,      \
-                           p.graphs_per_seq(), budget, seq_len, p.S, n_cand, idx, idx_stride,  \
-                           idx_len, num_sel, cand, selected, err);                             \
-        return hipGetLastError();                                                              \
+#define CKV_SEL_CASE(I)                                                                         \
+    if (ipt <= I) {                                                                             \
+        hipLaunchKernelGGL(select_kernel<I>, dim3(p.NG()), dim3(kSelThreads), 0, st, scores,    \
+                           gr.num_comms, gr.comm_start, gr.comm_size, gr.members, p.Cmax,       \
+                           p.graphs_per_seq(), budget, seq_len, p.S, n_cand, idx, idx_stride,   \
+                           idx_len, num_sel, cand, selected, err);                              \
+        return hipGetLastError();                                                               \
     }
-    CKV_SEL_CASE(1) CKV_SEL_CASE(2) CKV_SEL_CASE(4)
+    CKV_SEL_CASE(1) CKV_SEL_CASE(2) CKV_SEL_CASE(3) CKV_SEL_CASE(4) CKV_SEL_CASE(6)
+    CKV_SEL_CASE(8)
 #undef CKV_SEL_CASE
     return hipErrorInvalidValue;
 }

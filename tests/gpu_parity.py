@@ -100,9 +100,10 @@ def compare_state(layer: Bd.DecodeLayer, st, wl):
             _fail(f"graph {g}: centroids differ, max relative norm error {float((na / nb).max()):.3e}")
 
 
-def run_parity(wl, steps=None, li=0, index_stride=None, log=print):
-    """Run `steps` decode steps of layer `li` on the GPU and in the oracle and
-    compare every step.  Returns a summary dict."""
+def run_parity(wl, steps=None, li=0, index_stride=None, fused=False, log=print):
+    """Run `steps` decode steps of layer `li` on the GPU (the four C-ABI calls, or
+    the fused ckv_decode_step) and in the oracle, and compare every step.
+    Returns a summary dict."""
     steps = wl.steps if steps is None else steps
     torch.cuda.synchronize()
     layer = Bd.decode_layer_from_workload(wl, li, index_stride=index_stride)
@@ -117,7 +118,10 @@ def run_parity(wl, steps=None, li=0, index_stride=None, log=print):
         q, kn, vn = L.q[t].contiguous(), L.k_new[t].contiguous(), L.v_new[t].contiguous()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        layer.step(q, kn, vn, wl.scale)
+        if fused:
+            layer.step_fused(q, kn, vn, wl.scale)
+        else:
+            layer.step(q, kn, vn, wl.scale)
         torch.cuda.synchronize()
         t_gpu += time.perf_counter() - t0
         err = int(layer.err.item())

@@ -48,11 +48,9 @@ def dims(**kw):
 
 def test_workspace_sizes(lib):
     ok = dims(B=4)
-    # counters (NG u32, padded) + partials NG*G*splits*(d+2) fp32; 4100 entries -> 17 splits
-    ng, g, splits = 32, 4, (4100 + 255) // 256
-    expect = (ng * 4 + 255) // 256 * 256 + ng * g * splits * (128 + 2) * 4
-    assert lib.ckv_workspace_size(C.byref(ok), 4100) == expect
-    assert lib.ckv_score_workspace_size(C.byref(ok)) == ng * 4 * 128 * 8
+    # partials NG*G*splits*(d+2) fp32; 4100 entries at 192 per split -> 22 splits
+    ng, g, splits = 32, 4, (4100 + 191) // 192
+    assert lib.ckv_workspace_size(C.byref(ok), 4100) == ng * g * splits * (128 + 2) * 4
     assert lib.ckv_workspace_size(C.byref(dims(d=96)), 4100) == 0
     assert lib.ckv_workspace_size(C.byref(ok), 0) == 0
     assert lib.ckv_workspace_size(None, 16) == 0
@@ -67,7 +65,7 @@ def test_bad_dims_rejected(lib, kw, status):
     d = dims(**kw)
     fake = C.c_void_p(0x1000)
     g = Bd.ckv_graphs(fake, fake, fake, fake, fake, fake)
-    r = lib.ckv_score_centroids(C.byref(d), fake, C.byref(g), 0.1, fake, fake, 1 << 30, None)
+    r = lib.ckv_score_centroids(C.byref(d), fake, C.byref(g), 0.1, fake, None)
     assert r == status
 
 
@@ -75,11 +73,9 @@ def test_null_pointers_and_small_workspace(lib):
     d = dims()
     fake = C.c_void_p(0x1000)
     g = Bd.ckv_graphs(fake, fake, fake, fake, fake, None)           # members missing
-    assert lib.ckv_score_centroids(C.byref(d), fake, C.byref(g), 0.1, fake, fake, 1 << 30,
-                                   None) == -1
+    assert lib.ckv_score_centroids(C.byref(d), fake, C.byref(g), 0.1, fake, None) == -1
     g = Bd.ckv_graphs(fake, fake, fake, fake, fake, fake)
-    assert lib.ckv_score_centroids(C.byref(d), fake, C.byref(g), 0.1, fake, fake, 16,
-                                   None) == -3
+    assert lib.ckv_score_centroids(C.byref(d), None, C.byref(g), 0.1, fake, None) == -1
     kv = Bd.ckv_kv(fake, fake, fake, 16, 8, 8, fake)
     assert lib.ckv_sparse_decode_attn(C.byref(d), fake, C.byref(kv), fake, 2052, fake, 0.1,
                                       fake, fake, 64, fake, None) == -3
@@ -93,7 +89,16 @@ def test_null_pointers_and_small_workspace(lib):
                           fake, None, fake, None) == -1
     assert lib.ckv_local_update(C.byref(d), fake, None, fake, 8, C.byref(g), C.byref(kv), fake,
                                 fake, None) == -1
-    assert lib.ckv_workspace_init(None, 16, None) == -1
+    big = Bd.ckv_kv(fake, fake, fake, 16, 8, 1 << 24, fake)          # 32-bit row index overflow
+    assert lib.ckv_sparse_decode_attn(C.byref(d), fake, C.byref(big), fake, 2052, fake, 0.1,
+                                      fake, fake, 1 << 30, fake, None) == -2
+    # fused step: workspace too small, n_cand out of range
+    assert lib.ckv_decode_step(C.byref(d), fake, fake, fake, C.byref(g), C.byref(kv), fake, 8,
+                               0.1, fake, fake, 2052, fake, None, fake, None, fake, fake, fake,
+                               64, fake, None, None) == -3
+    assert lib.ckv_decode_step(C.byref(d), fake, fake, fake, C.byref(g), C.byref(kv), fake, 0,
+                               0.1, fake, fake, 2052, fake, None, fake, None, fake, fake, fake,
+                               1 << 30, fake, None, None) == -1
 
 
 def test_status_strings(lib):

@@ -30,17 +30,21 @@ def _case(name):
     print(f"\n[case] {name}", flush=True)
 
 
-@pytest.mark.parametrize("cfg,kw", [
+REDUCED = [
     (0, dict()),
     (1, dict(context=8192, steps=4)),
     (2, dict(context=8192, steps=3)),
     (3, dict(context=16384, steps=3)),
     (4, dict(context=16384, steps=2, layers=2, batch=6)),
-])
-def test_parity_reduced(cfg, kw):
-    _case(f"cfg{cfg} {kw}")
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["four-calls", "fused-step"])
+@pytest.mark.parametrize("cfg,kw", REDUCED)
+def test_parity_reduced(cfg, kw, fused):
+    _case(f"cfg{cfg} {kw} fused={fused}")
     wl = I.make_workload(cfg, device="cuda", **kw)
-    run_parity(wl, li=len(wl.layers) - 1)
+    run_parity(wl, li=len(wl.layers) - 1, fused=fused)
 
 
 def test_parity_budget_zero_sinks_only():
@@ -74,7 +78,8 @@ def test_parity_single_candidate():
     run_parity(wl)
 
 
-def test_parity_exact_score_ties():
+@pytest.mark.parametrize("fused", [False, True], ids=["four-calls", "fused-step"])
+def test_parity_exact_score_ties(fused):
     """Duplicated centroids give exactly equal scores; the (score desc, id asc)
     order must be reproduced bit for bit."""
     _case("tied scores")
@@ -82,14 +87,15 @@ def test_parity_exact_score_ties():
     cen = wl.layers[0].centroids
     C = int(wl.layers[0].num_comms.min())
     cen[:, 1:C:2] = cen[:, 0:C - 1:2]
-    run_parity(wl)
+    run_parity(wl, fused=fused)
 
 
-def test_parity_zero_query():
+@pytest.mark.parametrize("fused", [False, True], ids=["four-calls", "fused-step"])
+def test_parity_zero_query(fused):
     _case("q = 0")
     wl = I.make_workload(1, device="cuda", context=4096, steps=2)
     wl.layers[0].q.zero_()
-    run_parity(wl)
+    run_parity(wl, fused=fused)
 
 
 def test_capacity_overflow_is_flagged():
@@ -129,15 +135,17 @@ def test_unmapped_page_is_flagged_and_skipped():
 @pytest.mark.parametrize("cfg,kw", [
     (1, dict(steps=16)),
     (2, dict(steps=8)),
-    (3, dict(steps=2)),
+    (3, dict(steps=3)),
 ])
 def test_parity_full_size(cfg, kw):
+    """The configurations' real shapes, in the launch configuration the benchmark
+    times (the fused decode step)."""
     _case(f"full size cfg{cfg} {kw}")
     wl = I.make_workload(cfg, device="cuda", **kw)
-    run_parity(wl)
+    run_parity(wl, fused=True)
 
 
 def test_parity_full_size_ragged_paged():
     _case("full size cfg4, 1 of 36 layers")
-    wl = I.make_workload(4, device="cuda", steps=1, layers=1)
-    run_parity(wl)
+    wl = I.make_workload(4, device="cuda", steps=2, layers=1)
+    run_parity(wl, fused=True)
