@@ -10,10 +10,12 @@ budget 4096 tokens + 4 sinks.
 Timing protocol (cold): before every timed step the script reads through a
 1 GiB scrub buffer (a reduction, so the caches end up holding clean scrub data)
 so that neither the 4 MB L2s nor the 256 MB MALL hold the previous step's
-centroids, lists or KV rows; the step itself is bracketed by HIP
-events on the stream the kernels run on, per kernel.  `value` = tokens (decode
-tokens of all sequences) / sum of the step times.  The warm back-to-back rate is
-reported beside it.  Inputs are resident in HBM before timing starts.
+centroids, lists or KV rows; the step itself is bracketed by HIP events on the
+stream the kernels run on (launch gaps included), and each kernel carries its own
+start / stop events bound to its execution.  `value` = tokens (decode tokens of
+all sequences) / sum of the bracketed step times; the roofline uses the bound
+kernel duration.  `--warm` drops the scrub (back-to-back steps).  Inputs are
+resident in HBM before timing starts.
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
@@ -64,25 +66,32 @@ def step_bytes(layer: Bd.DecodeLayer, idx_len: np.ndarray, elem: int):
     upd = layer.NG * (layer.M * d * 4 + layer.M * 4 + d * 4 * 2) + \
         layer.B * layer.Hkv * 2 * d * elem * 2
     merge = layer.B * layer.Hq * d * 4
-    return dict(score=score, select_update=select + upd, attn=attn, merge=merge)
+    return dict(score=score, select=select, attn_update=attn + upd, merge=merge), attn
 
 
-KERNELS = ["score", "select_update", "attn", "merge"]
+KERNELS = ["score", "select", "attn_update", "merge"]
 
 
 class Timed:
-    """One layer's fused decode step (ckv_decode_step, 4 kernels) with HIP events
-    recorded by the library between its kernels, on the stream they run on."""
+    """One layer's fused decode step (ckv_decode_step, 4 kernels) on torch's current
+    stream: a pair of events around the whole step (launch gaps included) and the
+    library's per-kernel start / stop events (kernel execution only)."""
 
     def __init__(self, layer):
         self.layer = layer
-        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+        self.step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
 
-    def run(self, q, kn, vn, scale):
-        self.layer.step_fused(q, kn, vn, scale, events=self.ev)
+    def run(self, q, kn, vn, scale, per_kernel: bool):
+        self.step_ev[0].record()
+        self.layer.step_fused(q, kn, vn, scale, events=self.ev if per_kernel else None)
+        self.step_ev[1].record()
+
+    def step_ms(self):
+        return self.step_ev[0].elapsed_time(self.step_ev[1])
 
     def times_ms(self):
-        return [self.ev[i].elapsed_time(self.ev[i + 1]) for i in range(4)]
+        return [self.ev[2 * i].elapsed_time(self.ev[2 * i + 1]) for i in range(4)]
 
 
 def build_layers(wl, index_stride):
@@ -141,7 +150,9 @@ def main():
     Bd.load()
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    T = args.warmup + args.steps
+    # warmup, then K steps timed as a whole (value), then K steps with per-kernel
+    # events (roofline); the per-kernel events are kept out of the value pass
+    T = args.warmup + 2 * args.steps
     spec = I.CONFIGS[args.config]
     t0 = time.perf_counter()
     wl = I.make_workload(args.config, args.seed, device=dev, steps=T, layers=args.layers)
@@ -170,26 +181,34 @@ def main():
     qkv = [(L.q, L.k_new, L.v_new) for L in wl.layers]
     kernel_ms = np.zeros(4)
     kernel_bytes = {k: 0 for k in KERNELS}
-    step_ms = []
+    attn_only_bytes = 0
+    step_ms, step_ms_instr = [], []
+    value_bytes = 0
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for t in range(T):
-        timed = t >= args.warmup
+        phase = 0 if t < args.warmup else (1 if t < args.warmup + args.steps else 2)
         tot = 0.0
         for li, (tm, (q, kn, vn)) in enumerate(zip(timers, qkv)):
             if not args.warm:
                 scrub_sum = scrub.sum()               # cold caches, outside the events
-            tm.run(q[t], kn[t], vn[t], wl.scale)
+            tm.run(q[t], kn[t], vn[t], wl.scale, per_kernel=phase == 2)
             torch.cuda.synchronize()
-            if timed:
-                ms = np.array(tm.times_ms())
-                kernel_ms += ms
-                tot += ms.sum()
+            if phase:
+                tot += tm.step_ms()
                 idx_len = tm.layer.index_len.cpu().numpy()
-                for k, v in step_bytes(tm.layer, idx_len, elem).items():
-                    kernel_bytes[k] += v
-        if timed:
+                by, ab = step_bytes(tm.layer, idx_len, elem)
+                if phase == 1:
+                    value_bytes += sum(by.values())
+                else:
+                    kernel_ms += np.array(tm.times_ms())
+                    for k, v in by.items():
+                        kernel_bytes[k] += v
+                    attn_only_bytes += ab
+        if phase == 1:
             step_ms.append(tot)
+        elif phase == 2:
+            step_ms_instr.append(tot)
         if t == 0 or (t + 1) % 10 == 0:
             log(f"[bench] step {t + 1}/{T}")
     wall = time.perf_counter() - wall0
@@ -201,12 +220,12 @@ def main():
     total_ms = float(np.sum(step_ms))
     toks = wl.B * K
     value = toks / (total_ms / 1e3)
-    all_bytes = sum(kernel_bytes.values())
+    all_bytes = value_bytes
     names = KERNELS
     per_kernel = {n: dict(ms_per_launch=kernel_ms[i] / (K * len(layers)),
                           gbs=kernel_bytes[n] / (kernel_ms[i] / 1e3) / 1e9 if kernel_ms[i] else None)
                   for i, n in enumerate(names)}
-    attn_gbs = per_kernel["attn"]["gbs"]
+    attn_gbs = per_kernel["attn_update"]["gbs"]
     res = {
         "metric": "sparse decode attention tokens/s + achieved HBM GB/s at 128K, Qwen3-8B shape",
         "value": value,
@@ -233,10 +252,12 @@ def main():
         "path_gbs": all_bytes / (total_ms / 1e3) / 1e9,
         "path_frac_hbm": all_bytes / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         "bytes_per_step": all_bytes / K,
+        "ms_per_step_with_kernel_events": float(np.mean(step_ms_instr)),
         "kernels": per_kernel,
+        "attn_share_of_attn_update_bytes": attn_only_bytes / kernel_bytes["attn_update"],
         "wall_s_timed_loop": wall,
         "roofline": {
-            "kernel": "attn_kernel (indexed split-K flash-decode, partials)",
+            "kernel": "attn_kernel (indexed split-K flash-decode partials + local update)",
             "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": attn_gbs / HBM_PEAK_GBS if attn_gbs else None, "traffic": None,
         },

@@ -189,15 +189,17 @@ CKV_API ckv_status ckv_local_update(const ckv_dims *dims, const void *k_new, con
                             void *stream);
 
 /*
- * One whole decode step, the four operations above in 4 kernel launches instead
- * of 5: scoring; selection + compaction; sparse attention (split partials); and
- * one launch that merges the partials (one workgroup per graph) and runs the
- * local update with the seq_len advance (one workgroup per sequence).  Arguments
- * and results are those of the four calls (num_selected and selected may be
- * NULL), and every result equals the sequence
+ * One whole decode step, the four operations above in 4 kernel launches:
+ * scoring; selection + compaction; sparse attention (split partials) with the
+ * local update running in extra workgroups of the same launch (attention reads
+ * neither centroids, member lists nor row n); and the split merge with the
+ * seq_len advance.  Arguments and results are those of the four calls
+ * (num_selected and selected may be NULL), and every result equals the sequence
  *   ckv_score_centroids; ckv_select; ckv_sparse_decode_attn; ckv_local_update.
- * events: NULL, or 5 hipEvent_t (as void*) recorded on `stream` before the first
- * kernel and after each of the 4 kernels, for per-kernel timing.
+ * events: NULL, or 8 hipEvent_t (as void*) created with timing enabled: the
+ * start / stop pair of each of the 4 kernels in the order above, bound to the
+ * kernel's own execution (hipExtLaunchKernelGGL), so hipEventElapsedTime of a
+ * pair is that kernel's duration without launch gaps.
  */
 CKV_API ckv_status ckv_decode_step(const ckv_dims *dims, const void *q, const void *k_new,
                                    const void *v_new, const ckv_graphs *graphs, const ckv_kv *kv,

@@ -166,14 +166,17 @@ def ckv_local_update(dims, k_new, v_new, cand, n_cand, graphs, kv, assigned, err
 def ckv_decode_step(dims, q, k_new, v_new, graphs, kv, budget, n_cand, scale, scores,
                     index_list, index_len, num_selected, cand, selected, assigned, out, ws,
                     err_flag, events=None, stream=None):
-    """events: None or 5 torch.cuda.Event(enable_timing=True), recorded before the
-    first kernel and after each of the 4 kernels."""
+    """events: None or 8 torch.cuda.Event(enable_timing=True): the start / stop pair
+    of each of the 4 kernels (score, select, attention + update, merge), bound to
+    the kernels' own execution."""
     ev = None
     if events is not None:
+        if len(events) != 8:
+            raise CkvError("ckv_decode_step takes 8 timing events")
         for e in events:
             if e.cuda_event == 0:        # torch creates the HIP event at first record
                 e.record()
-        ev = (C.c_void_p * 5)(*[e.cuda_event for e in events])
+        ev = (C.c_void_p * 8)(*[e.cuda_event for e in events])
     _check(load().ckv_decode_step(C.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new),
                                   C.byref(graphs), C.byref(kv), _ptr(budget), n_cand, scale,
                                   _ptr(scores), _ptr(index_list), index_list.shape[1],

@@ -133,10 +133,10 @@ ckv_status ckv_sparse_decode_attn(const ckv_dims *dims, const void *q, const ckv
     hipStream_t st = static_cast<hipStream_t>(stream);
     if ((s = hip_status(ckv::launch_attn_partials(p, q, *kv, index_list, index_stride, index_len,
                                                   scale, static_cast<float *>(ws), err_flag,
-                                                  st))) != CKV_OK)
+                                                  nullptr, st))) != CKV_OK)
         return s;
-    return hip_status(ckv::launch_attn_merge(p, index_len, index_stride, out,
-                                             static_cast<float *>(ws), st));
+    return hip_status(
+        ckv::launch_attn_merge(p, index_stride, out, static_cast<float *>(ws), nullptr, st));
 }
 
 ckv_status ckv_local_update(const ckv_dims *dims, const void *k_new, const void *v_new,
@@ -173,30 +173,29 @@ ckv_status ckv_decode_step(const ckv_dims *dims, const void *q, const void *k_ne
     if ((s = check_splits(p, index_stride)) != CKV_OK) return s;
     if (!ws || ws_bytes < ckv_workspace_size(dims, index_stride)) return CKV_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    auto mark = [&](int i) -> ckv_status {
-        if (!events) return CKV_OK;
-        return hip_status(hipEventRecord(static_cast<hipEvent_t>(events[i]), st));
+    // launch k's timing events, bound to the kernel's own start and end
+    auto timed = [&](int k) {
+        Problem t = p;
+        if (events) {
+            t.ev_start = static_cast<hipEvent_t>(events[2 * k]);
+            t.ev_stop = static_cast<hipEvent_t>(events[2 * k + 1]);
+        }
+        return t;
     };
-    if ((s = mark(0)) != CKV_OK) return s;
-    if ((s = hip_status(ckv::launch_score(p, q, *graphs, (double)scale, scores, st))) != CKV_OK)
+    if ((s = hip_status(ckv::launch_score(timed(0), q, *graphs, (double)scale, scores, st))) !=
+        CKV_OK)
         return s;
-    if ((s = mark(1)) != CKV_OK) return s;
-    if ((s = hip_status(ckv::launch_select(p, scores, *graphs, budget, kv->seq_len, n_cand,
+    if ((s = hip_status(ckv::launch_select(timed(1), scores, *graphs, budget, kv->seq_len, n_cand,
                                            index_list, index_stride, index_len, num_selected,
                                            cand, selected, err_flag, st))) != CKV_OK)
         return s;
-    if ((s = mark(2)) != CKV_OK) return s;
-    if ((s = hip_status(ckv::launch_attn_partials(p, q, *kv, index_list, index_stride, index_len,
-                                                  scale, static_cast<float *>(ws), err_flag,
-                                                  st))) != CKV_OK)
+    const ckv::UpdateSpec upd{k_new, v_new, cand, n_cand, graphs, assigned};
+    if ((s = hip_status(ckv::launch_attn_partials(timed(2), q, *kv, index_list, index_stride,
+                                                  index_len, scale, static_cast<float *>(ws),
+                                                  err_flag, &upd, st))) != CKV_OK)
         return s;
-    if ((s = mark(3)) != CKV_OK) return s;
-    if ((s = hip_status(ckv::launch_merge_update(p, index_len, index_stride, out,
-                                                 static_cast<float *>(ws), k_new, v_new, cand,
-                                                 n_cand, *graphs, *kv, assigned, err_flag, st))) !=
-        CKV_OK)
-        return s;
-    return mark(4);
+    return hip_status(ckv::launch_attn_merge(timed(3), index_stride, out,
+                                             static_cast<float *>(ws), kv->seq_len, st));
 }
 
 const char *ckv_status_string(ckv_status status) {

@@ -29,7 +29,8 @@
 //   per head.
 // * The merge (next launch, so no device-wide fences are needed) combines the
 //   partials: m* = max m_s, l = sum l_s 2^(m_s-m*), o = sum acc_s 2^(m_s-m*) / l.
-//   In the fused decode step the same launch also runs the local update.
+// * In the fused decode step grid row 0 holds extra workgroups, one wave per
+//   graph, that run the local update while the other workgroups stream K/V.
 #include "ckv_device.h"
 #include "ckv_internal.h"
 #include "update_rule.h"
@@ -99,13 +100,27 @@ __device__ __forceinline__ float qk_part<float, 4>(const uint32_t (&)[2], const 
     return s;
 }
 
-template <typename T, int D, int GH>
+// Fused decode step: the local update runs in extra workgroups of this launch.
+struct UpdateArgs {
+    const void *k_new, *v_new;
+    const int32_t *cand;
+    int M;
+    float *cent;
+    const int32_t *num_comms, *comm_start;
+    int32_t *comm_size;
+    const int32_t *comm_cap;
+    int32_t *members;
+    int Cmax, NG;
+    int32_t *assigned;
+};
+
+template <typename T, int D, int GH, bool WITH_UPDATE>
 __global__ __launch_bounds__(256) void attn_kernel(
-    const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
+    const T *__restrict__ q, T *__restrict__ kc, T *__restrict__ vc,
     const int32_t *__restrict__ page_table, int log2ps, int max_pages, int num_pages,
-    const int32_t *__restrict__ seq_len, const int32_t *__restrict__ idx, int idx_stride,
+    int32_t *__restrict__ seq_len, const int32_t *__restrict__ idx, int idx_stride,
     const int32_t *__restrict__ idx_len, int Hq, int Hkv, int gpk, float scale_log2,
-    float *__restrict__ part, int max_splits, int32_t *__restrict__ err) {
+    float *__restrict__ part, int max_splits, int32_t *__restrict__ err, UpdateArgs u) {
     constexpr int EPL = 16 / sizeof(T);     // row elements per lane
     constexpr int LPR = D / EPL;            // lanes per row
     constexpr int RPW = kWave / LPR;        // rows per wave-wide load
@@ -123,9 +138,27 @@ __global__ __launch_bounds__(256) void attn_kernel(
     __shared__ float s_l[kAttnWaves][GH];
     __shared__ float s_acc[kAttnWaves][GH][D];
 
+    if constexpr (WITH_UPDATE) {
+        // grid row 0: the local update, one wave per graph (dispatched first, so it
+        // runs under the K/V stream of the attention workgroups); seq_len advances
+        // in the merge launch
+        if (blockIdx.y == 0) {
+            __shared__ __align__(16) float s_upd[kAttnWaves * kUpdLdsFloats(D)];
+            const int w = threadIdx.x / kWave;
+            const size_t gu = (size_t)blockIdx.x * kAttnWaves + w;
+            if (gu < u.NG)
+                graph_update<T, D>(gu, static_cast<const T *>(u.k_new),
+                                   static_cast<const T *>(u.v_new), u.cand, u.M, u.cent,
+                                   u.num_comms, u.comm_start, u.comm_size, u.comm_cap, u.members,
+                                   u.Cmax, Hkv, gpk, kc, vc, page_table, log2ps, max_pages,
+                                   num_pages, seq_len, u.assigned, err,
+                                   s_upd + w * kUpdLdsFloats(D));
+            return;
+        }
+    }
     const int NG = gridDim.x;
     const int g = graph_of_column(blockIdx.x, NG, gpk);
-    const int split = blockIdx.y;
+    const int split = (int)blockIdx.y - (WITH_UPDATE ? 1 : 0);
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
@@ -135,7 +168,16 @@ __global__ __launch_bounds__(256) void attn_kernel(
     const int h0 = kvh * G + (gpk == 1 ? 0 : g % gpk);
     const int len = min(idx_len[g], idx_stride);
     const int nsplit = (len + CH - 1) / CH;
-    if (split >= nsplit) return;
+    if (split >= nsplit) {
+        // an empty split still marks its partial (weight 0) so the merge can read
+        // every split without knowing the list length
+        if (tid < GH) {
+            float *pp = part + (((size_t)g * GH + tid) * max_splits + split) * (D + 2);
+            pp[0] = -__builtin_inff();
+            pp[1] = 0.f;
+        }
+        return;
+    }
     // balanced cut of the list into nsplit chunks
     const int t_begin = (int)(((long long)len * split) / nsplit);
     const int t_end = (int)(((long long)len * (split + 1)) / nsplit);
@@ -204,6 +246,10 @@ __global__ __launch_bounds__(256) void attn_kernel(
     for (int i = 0; i < NLD; ++i)
         vr[i] = *reinterpret_cast<const uint4 *>(vc + (size_t)(rows[i] < 0 ? 0 : rows[i]) * D +
                                                  ls * EPL);
+    // all 2*NLD row loads stay in flight together: without this fence the
+    // scheduler sinks most of them below the first softmax batch, which splits
+    // the gather into dependent round trips
+    __builtin_amdgcn_sched_barrier(0);
 
     // online softmax over batches of kSub loads; m, l, acc are per row slot
     float m[GH], l[GH], acc[GH][EPL];
@@ -305,13 +351,16 @@ __global__ __launch_bounds__(256) void attn_kernel(
     }
 }
 
-// Merge of one graph's split partials into out.  The per-split weights
-// 2^(m_s - m*) / l are formed once in LDS (s_w, GH*max_splits floats); every output
-// element then sums its nsplit partial values with all loads of a batch in flight.
+// Merge of one graph's split partials into out (m* = max m_s, weights
+// 2^(m_s - m*) / sum_s l_s 2^(m_s - m*)).  Every split slot holds a valid (m, l)
+// -- empty splits carry m = -inf -- so all loads are issued at once, without first
+// reading the list length; acc values of weight-0 splits are never used.
 template <int D, int GH>
-__device__ __forceinline__ void merge_graph(int g, const int32_t *__restrict__ idx_len, int idx_stride, int chunk,
-                            int Hq, int Hkv, int gpk, float *__restrict__ out,
-                            const float *__restrict__ part, int max_splits, float *s_w) {
+__device__ __forceinline__ void merge_graph(int g, int Hq, int Hkv, int gpk,
+                                            float *__restrict__ out,
+                                            const float *__restrict__ part, int max_splits,
+                                            float *s_w) {
+    constexpr int kBatch = 32;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
@@ -319,118 +368,101 @@ __device__ __forceinline__ void merge_graph(int g, const int32_t *__restrict__ i
     const int b = g / (Hkv * gpk);
     const int kvh = (g / gpk) % Hkv;
     const int h0 = kvh * G + (gpk == 1 ? 0 : g % gpk);
-    const int len = min(idx_len[g], idx_stride);
-    const int nsplit = (len + chunk - 1) / chunk;
     const float *pbase = part + ((size_t)g * GH * max_splits) * (D + 2);
-    for (int h = w; h < GH; h += blockDim.x / kWave) {  // weights: one wave per head
-        const float *ph = pbase + (size_t)h * max_splits * (D + 2);
+    // this thread's output element and the first batch of its partial values
+    const int t0 = tid < GH * D ? tid : 0;
+    const int h = t0 / D, i = t0 % D;
+    const float *pa = pbase + (size_t)h * max_splits * (D + 2) + 2 + i;
+    float x[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) x[k] = k < max_splits ? pa[(size_t)k * (D + 2)] : 0.f;
+    // weights: one wave per head
+    for (int hh = w; hh < GH; hh += blockDim.x / kWave) {
+        const float *ph = pbase + (size_t)hh * max_splits * (D + 2);
         float mm = -__builtin_inff();
-        for (int s = lane; s < nsplit; s += kWave) mm = fmaxf(mm, ph[(size_t)s * (D + 2)]);
+        for (int s = lane; s < max_splits; s += kWave) mm = fmaxf(mm, ph[(size_t)s * (D + 2)]);
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
         float ll = 0.f;
-        for (int s = lane; s < nsplit; s += kWave) {
+        for (int s = lane; s < max_splits; s += kWave) {
             const float ms = ph[(size_t)s * (D + 2)];
             const float f = ms == -__builtin_inff() ? 0.f : fast_exp2(ms - mm);
-            s_w[h * max_splits + s] = f;
+            s_w[hh * max_splits + s] = f;
             ll += ph[(size_t)s * (D + 2) + 1] * f;
         }
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) ll += __shfl_xor(ll, off);
         const float inv = ll > 0.f ? 1.f / ll : 0.f;
-        for (int s = lane; s < nsplit; s += kWave) s_w[h * max_splits + s] *= inv;
+        for (int s = lane; s < max_splits; s += kWave) s_w[hh * max_splits + s] *= inv;
     }
     __syncthreads();
-    constexpr int kBatch = 16;
-    for (int t = tid; t < GH * D; t += blockDim.x) {
-        const int h = t / D, i = t % D;
-        const float *ph = pbase + (size_t)h * max_splits * (D + 2) + 2 + i;
-        float a = 0.f;
-        for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
-            float x[kBatch];
+    if (tid >= GH * D) return;
+    float a = 0.f;
+    for (int s0 = 0; s0 < max_splits; s0 += kBatch) {
+        if (s0 > 0) {
 #pragma unroll
             for (int k = 0; k < kBatch; ++k)
-                x[k] = s0 + k < nsplit ? ph[(size_t)(s0 + k) * (D + 2)] : 0.f;
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k)
-                if (s0 + k < nsplit) a += x[k] * s_w[h * max_splits + s0 + k];
+                x[k] = s0 + k < max_splits ? pa[(size_t)(s0 + k) * (D + 2)] : 0.f;
         }
-        out[((size_t)b * Hq + h0 + h) * D + i] = a;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (s0 + k < max_splits) {
+                const float wk = s_w[h * max_splits + s0 + k];
+                if (wk != 0.f) a += x[k] * wk;
+            }
+        }
     }
+    out[((size_t)b * Hq + h0 + h) * D + i] = a;
 }
 
+// One workgroup per graph; with seq_len_bump (fused decode step) the first graph
+// of every sequence also advances seq_len after the step's update has been made.
 template <int D, int GH>
-__global__ __launch_bounds__(512) void merge_kernel(const int32_t *__restrict__ idx_len,
-                                                    int idx_stride, int chunk, int Hq, int Hkv,
-                                                    int gpk, float *__restrict__ out,
+__global__ __launch_bounds__(512) void merge_kernel(int Hq, int Hkv, int gpk,
+                                                    float *__restrict__ out,
                                                     const float *__restrict__ part,
-                                                    int max_splits) {
+                                                    int max_splits,
+                                                    int32_t *__restrict__ seq_len_bump) {
     extern __shared__ float s_w[];
-    merge_graph<D, GH>(blockIdx.x, idx_len, idx_stride, chunk, Hq, Hkv, gpk, out, part,
-                       max_splits, s_w);
+    if (seq_len_bump && threadIdx.x == 0 && blockIdx.x % (Hkv * gpk) == 0)
+        seq_len_bump[blockIdx.x / (Hkv * gpk)] += 1;
+    merge_graph<D, GH>(blockIdx.x, Hq, Hkv, gpk, out, part, max_splits, s_w);
 }
 
-// Fused decode step, last kernel: workgroups 0..NG-1 merge the partials of graph
-// x; workgroups NG..NG+B-1 run the local update of sequence x-NG (every graph of
-// it, then seq_len += 1).  Attention has finished reading rows < n, so the update
-// may append row n here.
-struct UpdateArgs {
-    const void *k_new, *v_new;
-    const int32_t *cand;
-    int M;
-    float *cent;
-    const int32_t *num_comms, *comm_start;
-    int32_t *comm_size;
-    const int32_t *comm_cap;
-    int32_t *members;
-    int Cmax;
-    void *kc, *vc;
-    const int32_t *page_table;
-    int log2ps, max_pages, num_pages;
-    int32_t *seq_len, *assigned, *err;
-};
-
-template <typename T, int D, int GH>
-__global__ __launch_bounds__(512) void merge_update_kernel(const int32_t *__restrict__ idx_len,
-                                                           int idx_stride, int chunk, int Hq,
-                                                           int Hkv, int gpk, int NG,
-                                                           float *__restrict__ out,
-                                                           const float *__restrict__ part,
-                                                           int max_splits, UpdateArgs u) {
-    extern __shared__ float s_w[];
-    __shared__ __align__(16) float s_rows[(512 / kWave) * 3 * D];
-    if ((int)blockIdx.x < NG) {
-        merge_graph<D, GH>(blockIdx.x, idx_len, idx_stride, chunk, Hq, Hkv, gpk, out, part,
-                           max_splits, s_w);
-        return;
-    }
-    sequence_update<T, D>(blockIdx.x - NG, static_cast<const T *>(u.k_new),
-                          static_cast<const T *>(u.v_new), u.cand, u.M, u.cent, u.num_comms,
-                          u.comm_start, u.comm_size, u.comm_cap, u.members, u.Cmax, Hkv, gpk,
-                          static_cast<T *>(u.kc), static_cast<T *>(u.vc), u.page_table, u.log2ps,
-                          u.max_pages, u.num_pages, u.seq_len, u.assigned, u.err, s_rows);
-}
-
-template <typename T, int D, int GH>
+template <typename T, int D, int GH, bool UPD>
 static void launch_partials_t(const Problem &p, const void *q, const ckv_kv &kv,
                               const int32_t *idx, int idx_stride, const int32_t *idx_len,
-                              float scale, float *partials, int32_t *err, hipStream_t st) {
+                              float scale, float *partials, int32_t *err, const UpdateArgs &u,
+                              hipStream_t st) {
     const int ms = attn_max_splits(p, idx_stride);
-    hipLaunchKernelGGL((attn_kernel<T, D, GH>), dim3(p.NG(), ms), dim3(256), 0, st,
-                       static_cast<const T *>(q), static_cast<const T *>(kv.k),
-                       static_cast<const T *>(kv.v), kv.page_table, log2_pow2(kv.page_size),
+    hipExtLaunchKernelGGL((attn_kernel<T, D, GH, UPD>), dim3(p.NG(), ms + (UPD ? 1 : 0)),
+                          dim3(256), 0, st, p.ev_start, p.ev_stop, 0,
+                          static_cast<const T *>(q), static_cast<T *>(kv.k),
+                       static_cast<T *>(kv.v), kv.page_table, log2_pow2(kv.page_size),
                        kv.max_pages_per_seq, kv.num_pages, kv.seq_len, idx, idx_stride, idx_len,
-                       p.Hq, p.Hkv, p.gpk, scale * kLog2e, partials, ms, err);
+                       p.Hq, p.Hkv, p.gpk, scale * kLog2e, partials, ms, err, u);
 }
 
 hipError_t launch_attn_partials(const Problem &p, const void *q, const ckv_kv &kv,
                                 const int32_t *idx, int idx_stride, const int32_t *idx_len,
-                                float scale, float *partials, int32_t *err, hipStream_t st) {
+                                float scale, float *partials, int32_t *err, const UpdateSpec *upd,
+                                hipStream_t st) {
     const int GH = p.heads_per_graph();
+    UpdateArgs u{};
+    if (upd) {
+        u = UpdateArgs{upd->k_new, upd->v_new, upd->cand, upd->n_cand, upd->graphs->centroids,
+                       upd->graphs->num_comms, upd->graphs->comm_start, upd->graphs->comm_size,
+                       upd->graphs->comm_cap, upd->graphs->members, p.Cmax, p.NG(),
+                       upd->assigned};
+    }
 #define CKV_ATTN_CASE(TT, DT, DD, HH)                                                          \
     if (p.dtype == DT && p.D == DD && GH == HH) {                                              \
-        launch_partials_t<TT, DD, HH>(p, q, kv, idx, idx_stride, idx_len, scale, partials,     \
-                                      err, st);                                                \
+        if (upd)                                                                               \
+            launch_partials_t<TT, DD, HH, true>(p, q, kv, idx, idx_stride, idx_len, scale,     \
+                                                partials, err, u, st);                         \
+        else                                                                                   \
+            launch_partials_t<TT, DD, HH, false>(p, q, kv, idx, idx_stride, idx_len, scale,    \
+                                                 partials, err, u, st);                        \
         return hipGetLastError();                                                              \
     }
     CKV_ATTN_CASE(bf16_t, CKV_DT_BF16, 128, 1) CKV_ATTN_CASE(bf16_t, CKV_DT_BF16, 128, 2)
@@ -445,52 +477,21 @@ hipError_t launch_attn_partials(const Problem &p, const void *q, const ckv_kv &k
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_merge(const Problem &p, const int32_t *idx_len, int idx_stride, float *out,
-                             const float *partials, hipStream_t st) {
+hipError_t launch_attn_merge(const Problem &p, int idx_stride, float *out, const float *partials,
+                             int32_t *bump_seq_len, hipStream_t st) {
     const int GH = p.heads_per_graph();
     const int ms = attn_max_splits(p, idx_stride);
-    const int ch = attn_chunk(p.D, p.elem_bytes());
 #define CKV_MERGE_CASE(DD, HH)                                                                 \
     if (p.D == DD && GH == HH) {                                                               \
-        hipLaunchKernelGGL((merge_kernel<DD, HH>), dim3(p.NG()), dim3(512),                    \
-                           (size_t)HH * ms * sizeof(float), st, idx_len, idx_stride, ch, p.Hq, \
-                           p.Hkv, p.gpk, out, partials, ms);                                   \
+        hipExtLaunchKernelGGL((merge_kernel<DD, HH>), dim3(p.NG()), dim3(512),                 \
+                              (size_t)HH * ms * sizeof(float), st, p.ev_start, p.ev_stop, 0,   \
+                              p.Hq, p.Hkv, p.gpk, out,                                         \
+                           partials, ms, bump_seq_len);                                        \
         return hipGetLastError();                                                              \
     }
     CKV_MERGE_CASE(128, 1) CKV_MERGE_CASE(128, 2) CKV_MERGE_CASE(128, 4) CKV_MERGE_CASE(128, 8)
     CKV_MERGE_CASE(64, 1) CKV_MERGE_CASE(64, 2) CKV_MERGE_CASE(64, 4) CKV_MERGE_CASE(64, 8)
 #undef CKV_MERGE_CASE
-    return hipErrorInvalidValue;
-}
-
-hipError_t launch_merge_update(const Problem &p, const int32_t *idx_len, int idx_stride,
-                               float *out, const float *partials, const void *k_new,
-                               const void *v_new, const int32_t *cand, int n_cand,
-                               const ckv_graphs &gr, const ckv_kv &kv, int32_t *assigned,
-                               int32_t *err, hipStream_t st) {
-    const int GH = p.heads_per_graph();
-    const int ms = attn_max_splits(p, idx_stride);
-    const int ch = attn_chunk(p.D, p.elem_bytes());
-    UpdateArgs u{k_new, v_new, cand, n_cand, gr.centroids, gr.num_comms, gr.comm_start,
-                 gr.comm_size, gr.comm_cap, gr.members, p.Cmax, kv.k, kv.v, kv.page_table,
-                 log2_pow2(kv.page_size), kv.max_pages_per_seq, kv.num_pages, kv.seq_len,
-                 assigned, err};
-#define CKV_MU_CASE(TT, DT, DD, HH)                                                            \
-    if (p.dtype == DT && p.D == DD && GH == HH) {                                              \
-        hipLaunchKernelGGL((merge_update_kernel<TT, DD, HH>), dim3(p.NG() + p.B), dim3(512),   \
-                           (size_t)HH * ms * sizeof(float), st, idx_len, idx_stride, ch, p.Hq, \
-                           p.Hkv, p.gpk, p.NG(), out, partials, ms, u);                        \
-        return hipGetLastError();                                                              \
-    }
-    CKV_MU_CASE(bf16_t, CKV_DT_BF16, 128, 1) CKV_MU_CASE(bf16_t, CKV_DT_BF16, 128, 2)
-    CKV_MU_CASE(bf16_t, CKV_DT_BF16, 128, 4) CKV_MU_CASE(bf16_t, CKV_DT_BF16, 128, 8)
-    CKV_MU_CASE(bf16_t, CKV_DT_BF16, 64, 1) CKV_MU_CASE(bf16_t, CKV_DT_BF16, 64, 2)
-    CKV_MU_CASE(bf16_t, CKV_DT_BF16, 64, 4) CKV_MU_CASE(bf16_t, CKV_DT_BF16, 64, 8)
-    CKV_MU_CASE(float, CKV_DT_F32, 128, 1) CKV_MU_CASE(float, CKV_DT_F32, 128, 2)
-    CKV_MU_CASE(float, CKV_DT_F32, 128, 4) CKV_MU_CASE(float, CKV_DT_F32, 128, 8)
-    CKV_MU_CASE(float, CKV_DT_F32, 64, 1) CKV_MU_CASE(float, CKV_DT_F32, 64, 2)
-    CKV_MU_CASE(float, CKV_DT_F32, 64, 4) CKV_MU_CASE(float, CKV_DT_F32, 64, 8)
-#undef CKV_MU_CASE
     return hipErrorInvalidValue;
 }
 

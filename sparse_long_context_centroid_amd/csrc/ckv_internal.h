@@ -1,6 +1,7 @@
 // ckv_internal.h -- host-side problem description and kernel launchers of libckv.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -12,6 +13,9 @@ namespace ckv {
 // Validated copy of ckv_dims with derived sizes.
 struct Problem {
     int B, Hq, Hkv, D, gpk, Cmax, S, dtype;
+    // optional timing of the next launch: events bound to the kernel's own start
+    // and end (hipExtLaunchKernelGGL), null for none
+    hipEvent_t ev_start = nullptr, ev_stop = nullptr;
     int G() const { return Hq / Hkv; }
     int NG() const { return B * Hkv * gpk; }
     int heads_per_graph() const { return gpk == 1 ? G() : 1; }
@@ -53,16 +57,20 @@ hipError_t launch_select(const Problem &p, const float *scores, const ckv_graphs
                          const int32_t *budget, const int32_t *seq_len, int n_cand,
                          int32_t *idx, int idx_stride, int32_t *idx_len, int32_t *num_sel,
                          int32_t *cand, uint8_t *selected, int32_t *err, hipStream_t st);
+// Local update run inside the attention launch (fused decode step).
+struct UpdateSpec {
+    const void *k_new, *v_new;
+    const int32_t *cand;
+    int n_cand;
+    const ckv_graphs *graphs;
+    int32_t *assigned;
+};
 hipError_t launch_attn_partials(const Problem &p, const void *q, const ckv_kv &kv,
                                 const int32_t *idx, int idx_stride, const int32_t *idx_len,
-                                float scale, float *partials, int32_t *err, hipStream_t st);
-hipError_t launch_attn_merge(const Problem &p, const int32_t *idx_len, int idx_stride, float *out,
-                             const float *partials, hipStream_t st);
-hipError_t launch_merge_update(const Problem &p, const int32_t *idx_len, int idx_stride,
-                               float *out, const float *partials, const void *k_new,
-                               const void *v_new, const int32_t *cand, int n_cand,
-                               const ckv_graphs &gr, const ckv_kv &kv, int32_t *assigned,
-                               int32_t *err, hipStream_t st);
+                                float scale, float *partials, int32_t *err, const UpdateSpec *upd,
+                                hipStream_t st);
+hipError_t launch_attn_merge(const Problem &p, int idx_stride, float *out, const float *partials,
+                             int32_t *bump_seq_len, hipStream_t st);
 hipError_t launch_update(const Problem &p, const void *k_new, const void *v_new,
                          const int32_t *cand, int n_cand, const ckv_graphs &gr, const ckv_kv &kv,
                          int32_t *assigned, int32_t *err, hipStream_t st);

@@ -9,17 +9,24 @@
 // wave-wide load is one contiguous 1 KiB line of 64 float4 -- no cross-lane
 // reduction at all.  The inner products are accumulated in fp64 in element order:
 // each product of a bf16/fp32 query element with an fp32 centroid element is exact
-// in fp64, so the score is a deterministic function of the stored bytes.  The
-// group's queries are staged once per step as fp64 in [g][d/4][GH][4] order so the
-// per-element query values are wave-uniform and are fetched with scalar loads.
+// in fp64, so the score is a deterministic function of the stored bytes.  Each
+// workgroup widens the graph's queries to fp64 in LDS, [d/4][GH][4], so the
+// per-element query values are wave-uniform broadcast reads.
+#include <type_traits>
+
 #include "ckv_device.h"
 #include "ckv_internal.h"
 
 namespace ckv {
 
-constexpr int kScoreThreads = 256;
+// One wavefront per workgroup: many small workgroups spread the 1 KiB centroid
+// lines over every CU, and the query staging needs no workgroup barrier.
+constexpr int kScoreThreads = 64;
+// float4 chunks of a centroid in flight per lane: the next chunk's loads are
+// issued before the current one is consumed (two chunks of registers).
+constexpr int kScoreChunk = 8;
 
-// One workgroup = 256 consecutive communities of one graph, one per lane.  The
+// One workgroup = 64 consecutive communities of one graph, one per lane.  The
 // graph's GH query rows are widened to fp64 once into LDS, laid out [d/4][GH][4]
 // so that each step's 4*GH values are one contiguous broadcast read.
 template <typename T, int D, int GH>
@@ -27,52 +34,89 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const T *__restrict__ q, const float *__restrict__ cent, const int32_t *__restrict__ num_comms,
     const int32_t *__restrict__ comm_size, int Cmax, int Hq, int Hkv, int gpk, double scale,
     float *__restrict__ scores) {
-    __shared__ double sq[D * GH];
+    constexpr int KC = kScoreChunk;
+    static_assert((D / 4) % KC == 0, "whole chunks");
+    // lane j stages entries 4j..4j+3 of [d/4][GH][4]: elements 4k..4k+3 of head h,
+    // k = j / GH, h = j % GH, with one vector load
+    constexpr int NQ = (D * GH / 4 + kScoreThreads - 1) / kScoreThreads;
+    __shared__ double sq[NQ * kScoreThreads * 4];
     const int g = blockIdx.y;
-    const int C = min(num_comms[g], Cmax);
-    const int base = blockIdx.x * kScoreThreads;
-    if (base >= C) return;
-    const int c = base + threadIdx.x;
-    const bool live = c < C;
+    const int c0 = blockIdx.x * kScoreThreads + threadIdx.x;
+    const int c = min(c0, Cmax - 1);
     const int G = Hq / Hkv;
     const int b = g / (Hkv * gpk);
     const int kvh = (g / gpk) % Hkv;
     const int h0 = kvh * G + (gpk == 1 ? 0 : g % gpk);
-    // Stage the graph's queries in LDS before the centroid stream starts: a query
-    // load issued behind 32 KiB of centroid requests per wave would wait for the
-    // whole stream.
-    for (int t = threadIdx.x; t < D * GH; t += kScoreThreads) {
-        const int k = t / (GH * 4), h = (t / 4) % GH, e = t % 4;
-        sq[t] = (double)to_f32(q[((size_t)b * Hq + h0 + h) * D + k * 4 + e]);
+    // every load is issued before any result is waited for: the query chunk, the
+    // first centroid chunk, the size and the community count (the workgroup runs
+    // even past the graph's count, so that no load waits behind a branch)
+    using Q4 = typename std::conditional<sizeof(T) == 2, uint2, float4>::type;
+    Q4 qraw[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const int jq = min((int)threadIdx.x + j * kScoreThreads, D * GH / 4 - 1);
+        qraw[j] = *reinterpret_cast<const Q4 *>(q + ((size_t)b * Hq + h0 + jq % GH) * D +
+                                                (jq / GH) * 4);
+    }
+    const float4 *cp = reinterpret_cast<const float4 *>(cent) + (size_t)g * (D / 4) * Cmax + c;
+    float4 cur[KC];
+#pragma unroll
+    for (int k = 0; k < KC; ++k) cur[k] = cp[(size_t)k * Cmax];
+    const int sz = comm_size[(size_t)g * Cmax + c];
+    const int C = min(num_comms[g], Cmax);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        float e4[4];
+        if constexpr (sizeof(T) == 2) {
+            const uint2 w = reinterpret_cast<const uint2 &>(qraw[j]);
+            e4[0] = bf16_lo(w.x);
+            e4[1] = bf16_hi(w.x);
+            e4[2] = bf16_lo(w.y);
+            e4[3] = bf16_hi(w.y);
+        } else {
+            const float4 w = reinterpret_cast<const float4 &>(qraw[j]);
+            e4[0] = w.x;
+            e4[1] = w.y;
+            e4[2] = w.z;
+            e4[3] = w.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sq[(threadIdx.x + j * kScoreThreads) * 4 + e] = (double)e4[e];
     }
     __syncthreads();
-    const float4 *cp = reinterpret_cast<const float4 *>(cent) + (size_t)g * (D / 4) * Cmax +
-                       (live ? c : base);
-    float4 v[D / 4];
-#pragma unroll
-    for (int k = 0; k < D / 4; ++k) v[k] = cp[(size_t)k * Cmax];
-    const int sz = live ? comm_size[(size_t)g * Cmax + c] : 0;
 
     double acc[GH];
 #pragma unroll
     for (int h = 0; h < GH; ++h) acc[h] = 0.0;
+    // (kept rolled: unrolled, the compiler moves each load down to its use and the
+    // chunks' round trips serialise)
+#pragma unroll 1
+    for (int k0 = 0; k0 < D / 4; k0 += KC) {
+        float4 nxt[KC];
+        const int kn = min(k0 + KC, D / 4 - KC);  // the last pass reloads a chunk, unused
 #pragma unroll
-    for (int k = 0; k < D / 4; ++k) {
-        const double e0 = v[k].x, e1 = v[k].y, e2 = v[k].z, e3 = v[k].w;
+        for (int k = 0; k < KC; ++k) nxt[k] = cp[(size_t)(kn + k) * Cmax];
 #pragma unroll
-        for (int h = 0; h < GH; ++h) {
-            const double *qq = sq + (k * GH + h) * 4;
-            acc[h] = fma(qq[0], e0, acc[h]);
-            acc[h] = fma(qq[1], e1, acc[h]);
-            acc[h] = fma(qq[2], e2, acc[h]);
-            acc[h] = fma(qq[3], e3, acc[h]);
+        for (int kk = 0; kk < KC; ++kk) {
+            const int k = k0 + kk;
+            const double e0 = cur[kk].x, e1 = cur[kk].y, e2 = cur[kk].z, e3 = cur[kk].w;
+#pragma unroll
+            for (int h = 0; h < GH; ++h) {
+                const double *qq = sq + (k * GH + h) * 4;
+                acc[h] = fma(qq[0], e0, acc[h]);
+                acc[h] = fma(qq[1], e1, acc[h]);
+                acc[h] = fma(qq[2], e2, acc[h]);
+                acc[h] = fma(qq[3], e3, acc[h]);
+            }
         }
+#pragma unroll
+        for (int k = 0; k < KC; ++k) cur[k] = nxt[k];
     }
     double best = acc[0];
 #pragma unroll
     for (int h = 1; h < GH; ++h)
         if (acc[h] > best) best = acc[h];
-    if (live) scores[(size_t)g * Cmax + c] = sz > 0 ? (float)(best * scale) : -__builtin_inff();
+    if (c0 < C) scores[(size_t)g * Cmax + c] = sz > 0 ? (float)(best * scale) : -__builtin_inff();
 }
 
 // ---- layout helpers ---------------------------------------------------------------
@@ -104,9 +148,10 @@ __global__ void interleaved_to_rows_kernel(const float *__restrict__ cent, float
 template <typename T, int D, int GH>
 static void launch_score_t(const Problem &p, const void *q, const ckv_graphs &gr, double scale,
                            float *scores, hipStream_t st) {
-    hipLaunchKernelGGL((score_kernel<T, D, GH>),
-                       dim3((p.Cmax + kScoreThreads - 1) / kScoreThreads, p.NG()),
-                       dim3(kScoreThreads), 0, st, static_cast<const T *>(q), gr.centroids,
+    hipExtLaunchKernelGGL((score_kernel<T, D, GH>),
+                          dim3((p.Cmax + kScoreThreads - 1) / kScoreThreads, p.NG()),
+                          dim3(kScoreThreads), 0, st, p.ev_start, p.ev_stop, 0,
+                          static_cast<const T *>(q), gr.centroids,
                        gr.num_comms, gr.comm_size, p.Cmax, p.Hq, p.Hkv, p.gpk, scale, scores);
 }
 

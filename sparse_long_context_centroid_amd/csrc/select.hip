@@ -441,23 +441,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
         if (selected && c < Cmax) selected[(size_t)g * Cmax + c] = selA[i] ? 1 : 0;
     }
-    if (tid == 0) {
-        list_off[ksel] = total;
-        // order the candidates (at most M <= CKV_MAX_CAND) by (key desc, id asc)
+    if (tid == 0) list_off[ksel] = total;
+    if (tid < M) {
+        // the candidates (at most M <= CKV_MAX_CAND, unordered in LDS) go out in
+        // (key desc, id asc) order: each one's rank is the number it yields to
         const int nc = cand_n < M ? cand_n : M;
-        for (int a = 1; a < nc; ++a) {
-            const uint32_t kk = cand_key[a];
-            const int ii = cand_id[a];
-            int p = a - 1;
-            while (p >= 0 && (cand_key[p] < kk || (cand_key[p] == kk && cand_id[p] > ii))) {
-                cand_key[p + 1] = cand_key[p];
-                cand_id[p + 1] = cand_id[p];
-                --p;
-            }
-            cand_key[p + 1] = kk;
-            cand_id[p + 1] = ii;
+        if (tid < nc) {
+            const uint32_t kk = cand_key[tid];
+            const int ii = cand_id[tid];
+            int r = 0;
+            for (int j = 0; j < nc; ++j)
+                r += (cand_key[j] > kk || (cand_key[j] == kk && cand_id[j] < ii)) ? 1 : 0;
+            cand[(size_t)g * M + r] = ii;
+        } else {
+            cand[(size_t)g * M + tid] = -1;
         }
-        for (int a = nc; a < M; ++a) cand_id[a] = -1;
     }
     __syncthreads();
 
@@ -499,7 +497,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
     }
     if (overflow) set_err(err, CKV_DEVERR_INDEX_RANGE);
-    if (tid < M) cand[(size_t)g * M + tid] = cand_id[tid];
     if (tid == 0) {
         const int len = ns + total;
         idx_len[g] = len < idx_stride ? len : idx_stride;
@@ -515,7 +512,8 @@ hipError_t launch_select(const Problem &p, const float *scores, const ckv_graphs
     const int ipt = (p.Cmax + kSelThreads - 1) / kSelThreads;
 #define CKV_SEL_CASE(I)                                                                         \
     if (ipt <= I) {                                                                             \
-        hipLaunchKernelGGL(select_kernel<I>, dim3(p.NG()), dim3(kSelThreads), 0, st, scores,    \
+        hipExtLaunchKernelGGL(select_kernel<I>, dim3(p.NG()), dim3(kSelThreads), 0, st,         \
+                              p.ev_start, p.ev_stop, 0, scores,                                 \
                            gr.num_comms, gr.comm_start, gr.comm_size, gr.members, p.Cmax,       \
                            p.graphs_per_seq(), budget, seq_len, p.S, n_cand, idx, idx_stride,   \
                            idx_len, num_sel, cand, selected, err);                              \

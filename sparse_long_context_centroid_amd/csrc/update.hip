@@ -7,7 +7,8 @@
 //
 // One workgroup per sequence, so reading n and incrementing seq_len cannot race;
 // one wavefront per graph of the sequence (looping when there are more than 8).
-// The fused decode step does the same update inside the selection kernel instead.
+// The fused decode step runs the same update in extra workgroups of the attention
+// launch instead (attention reads neither centroids, member lists nor row n).
 #include "ckv_device.h"
 #include "ckv_internal.h"
 #include "update_rule.h"
@@ -23,7 +24,7 @@ __global__ __launch_bounds__(512) void update_kernel(
     int gpk, T *__restrict__ kc, T *__restrict__ vc, const int32_t *__restrict__ page_table,
     int log2ps, int max_pages, int num_pages, int32_t *__restrict__ seq_len,
     int32_t *__restrict__ assigned, int32_t *__restrict__ err) {
-    __shared__ __align__(16) float s_rows[8 * 3 * D];
+    __shared__ __align__(16) float s_rows[8 * kUpdLdsFloats(D)];
     sequence_update<T, D>(blockIdx.x, k_new, v_new, cand, M, cent, num_comms, comm_start,
                           comm_size, comm_cap, members, Cmax, Hkv, gpk, kc, vc, page_table,
                           log2ps, max_pages, num_pages, seq_len, assigned, err, s_rows);
