@@ -22,9 +22,10 @@
 // an id-ordered prefix of {key == T*}, where T* is the smallest key with
 // W(key > T*) <= budget (W = sum of sizes); W(key > T) does not increase with T,
 // so T* is found by a 4-ary search on the key, one size-weighted block reduction
-// per probe.  Both paths give exactly the (score desc, id asc) prefix.  The member lists of the kept communities are then
-// copied with one flat, balanced pass (each thread finds its community by binary
-// search over the compacted offsets), so all member loads are in flight at once.
+// per probe.  Both paths give exactly the (score desc, id asc) prefix.  The member
+// lists of the kept communities are then copied with one flat, balanced pass
+// (each thread finds its communities by lockstep binary searches over the
+// compacted offsets), so all member loads are in flight at once.
 #include "ckv_device.h"
 #include "ckv_internal.h"
 
@@ -79,15 +80,30 @@ __device__ __forceinline__ void block_sums(int (&v)[N], int *buf) {
     }
 }
 
+// Maximum of a float over the wavefront, as a wave-uniform value: DPP row shifts
+// (lanes without a source keep their own value), then the row totals carried by
+// row_bcast 15 / 31 into the last row.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_keep(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_keep<0x111>(x));       // row_shr:1
+    x = fmaxf(x, dpp_keep<0x112>(x));       // row_shr:2
+    x = fmaxf(x, dpp_keep<0x114>(x));       // row_shr:4
+    x = fmaxf(x, dpp_keep<0x118>(x));       // row_shr:8
+    x = fmaxf(x, dpp_keep<0x142, 0xA>(x));  // row_bcast:15
+    x = fmaxf(x, dpp_keep<0x143, 0xC>(x));  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
+}
+
 // Block maxima of two floats (all threads get both); `buf` holds 2*kSelWaves.
 __device__ __forceinline__ void block_max2(float (&v)[2], float *buf) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) v[j] = fmaxf(v[j], __shfl_xor(v[j], off));
-    }
+    for (int j = 0; j < 2; ++j) v[j] = wave_max(v[j]);
     if (lane == 0) {
         buf[w] = v[0];
         buf[kSelWaves + w] = v[1];
@@ -114,13 +130,9 @@ __device__ __forceinline__ void find_crossing(const int *hist, int cap, int *out
         h[i] = hist[lane * 4 + i];
         t += h[i];
     }
-    int s = t;  // suffix over lanes: sum over lanes >= this one
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_down(s, off);
-        if (lane + off < kWave) s += y;
-    }
-    const int total = __shfl(s, 0);
+    const int incl = wave_incl_scan(t);
+    const int s = __builtin_amdgcn_readlane(incl, kWave - 1) - incl + t;  // lanes >= this one
+    const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
     if (total <= cap) {
         if (lane == 0) {
             out[0] = -1;
@@ -215,8 +227,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __shared__ int cand_n;
     __shared__ int histA[256], histB[256], cross[4];
     __shared__ float fred[2 * kSelWaves];
-    __shared__ uint32_t pendA_key[kPend], pendB_key[kPend];
-    __shared__ int pendA_id[kPend], pendB_id[kPend], pendA_w[kPend];
+    // pending entries as (key, id, weight, -) so one LDS read fetches an entry
+    __shared__ int4 pendA[kPend], pendB[kPend];
     __shared__ bool pendA_sel[kPend], pendB_sel[kPend];
     __shared__ int pendA_n, pendB_n;
 
@@ -230,22 +242,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int Bt = budget[b] < 0 ? 0 : budget[b];
 
     // sizes, scores and member offsets of this thread's communities, all in flight
+    // (loaded unconditionally at clamped slots, so none waits for the community
+    // count; slots past it are masked afterwards)
     uint32_t key[IPT];
     float sc[IPT];
     int wt[IPT], cst[IPT];
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-        const int c = tid * IPT + i;
-        const size_t o = (size_t)g * Cmax + (c < C ? c : 0);
-        wt[i] = c < C ? comm_size[o] : 0;
-        sc[i] = c < C ? scores[o] : 0.f;
-        cst[i] = c < C ? comm_start[o] : 0;
+        const int c = min(tid * IPT + i, Cmax - 1);
+        const size_t o = (size_t)g * Cmax + c;
+        wt[i] = comm_size[o];
+        sc[i] = scores[o];
+        cst[i] = comm_start[o];
     }
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
         // valid keys are >= 1; 0 marks an empty or unused community
-        key[i] = wt[i] > 0 ? max(order_key(sc[i]), 1u) : 0u;
-        wt[i] = wt[i] > 0 ? wt[i] : 0;
+        const bool live = tid * IPT + i < C && wt[i] > 0;
+        wt[i] = live ? wt[i] : 0;
+        sc[i] = live ? sc[i] : 0.f;
+        key[i] = live ? max(order_key(sc[i]), 1u) : 0u;
     }
     if (tid == 0) cand_n = 0;
 
@@ -306,18 +322,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         selB[i] = bk[i] >= 0 && (bB < 0 || bk[i] > bB);
         if (bk[i] >= 0 && bk[i] == bA) {
             slotA[i] = atomicAdd(&pendA_n, 1);
-            if (slotA[i] < kPend) {
-                pendA_key[slotA[i]] = key[i];
-                pendA_id[slotA[i]] = tid * IPT + i;
-                pendA_w[slotA[i]] = wt[i];
-            }
+            if (slotA[i] < kPend)
+                pendA[slotA[i]] = make_int4((int)key[i], tid * IPT + i, wt[i], 0);
         }
         if (bk[i] >= 0 && bk[i] == bB) {
             slotB[i] = atomicAdd(&pendB_n, 1);
-            if (slotB[i] < kPend) {
-                pendB_key[slotB[i]] = key[i];
-                pendB_id[slotB[i]] = tid * IPT + i;
-            }
+            if (slotB[i] < kPend) pendB[slotB[i]] = make_int4((int)key[i], tid * IPT + i, 1, 0);
         }
     }
     __syncthreads();
@@ -325,25 +335,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     if (nPA <= kPend && nPB <= kPend) {
         // exact rank of each pending community among the pending ones, in the
         // (score desc, id asc) order: kept iff everything before it still fits
-        if (w == 0 && lane < nPA) {
-            const uint32_t k0 = pendA_key[lane];
-            const int i0 = pendA_id[lane];
-            int before = 0;
-            for (int j = 0; j < nPA; ++j) {
-                const uint32_t kj = pendA_key[j];
-                if (kj > k0 || (kj == k0 && pendA_id[j] < i0)) before += pendA_w[j];
+        if (w < 2) {
+            // wave 0 ranks the budget crossing (size weights), wave 1 the candidate
+            // crossing (unit weights)
+            const int4 *pend = w == 0 ? pendA : pendB;
+            const int np = w == 0 ? nPA : nPB;
+            if (lane < np) {
+                const int4 me = pend[lane];
+                const uint32_t k0 = (uint32_t)me.x;
+                int before = 0;
+#pragma unroll 4
+                for (int j = 0; j < np; ++j) {
+                    const int4 o = pend[j];
+                    const uint32_t kj = (uint32_t)o.x;
+                    before += (kj > k0 || (kj == k0 && o.y < me.y)) ? o.z : 0;
+                }
+                if (w == 0) pendA_sel[lane] = aboveA_b + before + me.z <= Bt;
+                else pendB_sel[lane] = aboveB_b + before + 1 <= M;
             }
-            pendA_sel[lane] = aboveA_b + before + pendA_w[lane] <= Bt;
-        }
-        if (w == 1 && lane < nPB) {
-            const uint32_t k0 = pendB_key[lane];
-            const int i0 = pendB_id[lane];
-            int before = 0;
-            for (int j = 0; j < nPB; ++j) {
-                const uint32_t kj = pendB_key[j];
-                if (kj > k0 || (kj == k0 && pendB_id[j] < i0)) before += 1;
-            }
-            pendB_sel[lane] = aboveB_b + before + 1 <= M;
         }
         __syncthreads();
 #pragma unroll
@@ -469,31 +478,43 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     // flat copy of the kept member lists: output slot p (0 <= p < total) belongs
     // to the compacted community e with list_off[e] <= p < list_off[e+1]
     constexpr int kBatch = 8;
+    int top = 1;  // largest power of two <= ksel (ksel >= 1 whenever total > 0)
+    while (top * 2 <= ksel) top *= 2;
     for (int p0 = 0; p0 < total; p0 += kBatch * kSelThreads) {
+        // last e with list_off[e] <= p, for the kBatch slots at once: the searches
+        // advance in lockstep, one LDS read per slot per halving step
+        int lo[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) lo[k] = 0;
+        for (int st = top; st > 0; st >>= 1) {
+            // branch-free: all kBatch LDS reads of a step are issued back to back
+            int v[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) v[k] = list_off[min(lo[k] + st, ksel - 1)];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const int p = p0 + k * kSelThreads + tid;
+                lo[k] = (lo[k] + st < ksel && v[k] <= p) ? lo[k] + st : lo[k];
+            }
+        }
         int src[kBatch];
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int p = p0 + k * kSelThreads + tid;
-            src[k] = -1;
-            if (p < total) {
-                int lo = 0, hi = ksel - 1;  // last e with list_off[e] <= p
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (list_off[mid] <= p) lo = mid; else hi = mid - 1;
-                }
-                src[k] = list_start[lo] + (p - list_off[lo]);
-            }
+            const int st0 = list_start[lo[k]], of0 = list_off[lo[k]];  // read unconditionally
+            src[k] = p < total ? st0 + (p - of0) : -1;
         }
+        // unconditional loads (slot 0 for idle lanes; total > 0 here, so the pool is
+        // not empty): loads inside branches make the compiler wait for every
+        // outstanding access, stores included, before each store
         int val[kBatch];
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) val[k] = src[k] >= 0 ? members[(size_t)src[k]] : 0;
+        for (int k = 0; k < kBatch; ++k) val[k] = members[(size_t)max(src[k], 0)];
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int o = ns + p0 + k * kSelThreads + tid;
-            if (src[k] >= 0) {
-                if (o < idx_stride) out[o] = val[k];
-                else overflow = true;
-            }
+            if (src[k] >= 0 && o < idx_stride) out[o] = val[k];
+            overflow |= src[k] >= 0 && o >= idx_stride;
         }
     }
     if (overflow) set_err(err, CKV_DEVERR_INDEX_RANGE);
