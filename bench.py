@@ -71,6 +71,30 @@ def step_bytes(layer: Bd.DecodeLayer, idx_len: np.ndarray, elem: int):
 
 KERNELS = ["score", "select", "attn_update", "merge"]
 
+PMC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_b4_ctx128k_pmc_traffic.txt")
+ATTN_SOURCES = ["attn.hip", "update_rule.h", "ckv_device.h", "ckv_internal.h"]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (calibrated against a plain copy), or None when the
+    summary is for another workload or the attention kernel's sources changed
+    since the counters were taken."""
+    import hashlib
+    if workload != "qwen3-8b-layer-b4-ctx128k-group" or not os.path.exists(PMC_FILE):
+        return None
+    txt = open(PMC_FILE).read()
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, "sparse_long_context_centroid_amd", "csrc", f), "rb").read())
+    traffic = sha = None
+    for line in txt.splitlines():
+        if line.startswith("roofline traffic of"):
+            traffic = int(line.rsplit(":", 1)[1])
+        elif line.startswith("source-sha256"):
+            sha = line.rsplit(":", 1)[1].strip()
+    return traffic if sha == h.hexdigest() else None
+
 
 class Timed:
     """One layer's fused decode step (ckv_decode_step, 4 kernels) on torch's current
@@ -259,7 +283,10 @@ def main():
         "roofline": {
             "kernel": "attn_kernel (indexed split-K flash-decode partials + local update)",
             "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": attn_gbs / HBM_PEAK_GBS if attn_gbs else None, "traffic": None,
+            "frac": attn_gbs / HBM_PEAK_GBS if attn_gbs else None,
+            "traffic": measured_traffic(spec.name),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes_per_launch": kernel_bytes["attn_update"] / (K * len(layers)),
         },
         "cpu_baseline": cpu,
     }
