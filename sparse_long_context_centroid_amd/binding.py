@@ -283,6 +283,9 @@ def decode_layer_from_workload(wl, li: int = 0, index_stride: Optional[int] = No
     L = wl.layers[li]
     if index_stride is None:
         index_stride = int(wl.S + wl.budget.max())
+    if tuple(L.comm_start.shape) != (wl.NG, wl.Cmax) or L.centroids.shape[1] != wl.Cmax:
+        raise CkvError(f"layer {li}: per-community arrays are not [NG, Cmax] = "
+                       f"[{wl.NG}, {wl.Cmax}]")
     return DecodeLayer(B=wl.B, Hq=wl.Hq, Hkv=wl.Hkv, d=wl.d, gpk=wl.gpk, S=wl.S,
                        dtype=wl.dtype, Cmax=wl.Cmax, M=wl.M, index_stride=index_stride,
                        page_size=wl.page_size, centroid_rows=L.centroids,

@@ -238,7 +238,11 @@ def make_workload(cfg: int | ConfigSpec, seed: Optional[int] = None, *, device: 
     for li in range(L):
         layer_objs.append(_make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G,
                                       gpk, page_table, num_pages, tdt, device))
-    Cmax = layer_objs[0].centroids.shape[1]
+    # one community stride for every layer: pad each layer's per-community arrays
+    # to the largest (padding columns are empty communities past num_comms)
+    Cmax = max(lo.centroids.shape[1] for lo in layer_objs)
+    for lo in layer_objs:
+        _pad_communities(lo, Cmax)
     return Workload(spec=spec, seed=seed, B=B, Hq=Hq, Hkv=Hkv, d=d, gpk=gpk, S=S, M=M,
                     dtype=spec.dtype, Cmax=Cmax, steps=T, page_size=ps, max_pages=max_pages,
                     num_pages=num_pages,
@@ -246,6 +250,19 @@ def make_workload(cfg: int | ConfigSpec, seed: Optional[int] = None, *, device: 
                     seq_len0=ns.astype(np.int32), budget=bud.astype(np.int32),
                     scale=float(np.float32(1.0 / math.sqrt(d))), layers=layer_objs,
                     device=device)
+
+
+def _pad_communities(layer: Layer, Cmax: int) -> None:
+    c0 = layer.centroids.shape[1]
+    if c0 == Cmax:
+        return
+    pad = Cmax - c0
+    layer.centroids = torch.cat(
+        [layer.centroids, layer.centroids.new_zeros((layer.centroids.shape[0], pad,
+                                                     layer.centroids.shape[2]))], dim=1)
+    for name in ("comm_start", "comm_size", "comm_cap"):
+        a = getattr(layer, name)
+        setattr(layer, name, np.concatenate([a, np.zeros((a.shape[0], pad), a.dtype)], axis=1))
 
 
 def _make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G, gpk, page_table,

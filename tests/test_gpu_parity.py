@@ -149,3 +149,11 @@ def test_parity_full_size_ragged_paged():
     _case("full size cfg4, 1 of 36 layers")
     wl = I.make_workload(4, device="cuda", steps=2, layers=1)
     run_parity(wl, fused=True)
+
+
+def test_parity_full_size_ragged_paged_deep_layer():
+    """A later layer of a multi-layer workload: every layer shares one community
+    stride, whatever its own partition sizes."""
+    _case("full size cfg4, layer 7 of 8")
+    wl = I.make_workload(4, device="cuda", steps=2, layers=8)
+    run_parity(wl, li=7, fused=True)
