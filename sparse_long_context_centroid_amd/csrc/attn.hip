@@ -68,6 +68,32 @@ __device__ __forceinline__ int graph_of_column(int x, int NG, int gpk) {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+struct OpAdd {
+    __device__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+    __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+// op(x[L], x[L ^ OFF]) in every lane L (the same value in both lanes of a pair),
+// for OFF = 8 (DPP rotate by 8 inside a 16-lane row), 16 or 32 (gfx950 lane-swap
+// instructions: after the swap the two registers hold the even and the odd
+// 16-lane rows, resp. the low and the high 32 lanes, of x in both halves).
+template <int OFF, typename Op>
+__device__ __forceinline__ float pair_op(float x, Op op) {
+    static_assert(OFF == 8 || OFF == 16 || OFF == 32, "pair distance");
+    const uint32_t u = __float_as_uint(x);
+    if constexpr (OFF == 8) {
+        return op(x, __uint_as_float(__builtin_amdgcn_update_dpp(u, u, 0x128, 0xF, 0xF, false)));
+    } else if constexpr (OFF == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+}
+
 // Partial q.K over this lane's EPL elements of a row, for one head.
 template <typename T, int EPL>
 __device__ __forceinline__ float qk_part(const uint32_t (&qp)[EPL / 2 > 0 ? EPL / 2 : 1],
@@ -297,23 +323,32 @@ __global__ __launch_bounds__(256) void attn_kernel(
             }
         }
     }
-    // merge the RPW row slots of the wave (same dims, disjoint tokens, own maxima)
+    // merge the RPW row slots of the wave (same dims, disjoint tokens, own maxima);
+    // lanes L and L^off pair up with VALU lane swaps, no LDS round trips
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
         float mm = m[h];
-#pragma unroll
-        for (int off = LPR; off < kWave; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
+        if constexpr (LPR <= 8) mm = pair_op<8>(mm, OpMax{});
+        if constexpr (LPR <= 16) mm = pair_op<16>(mm, OpMax{});
+        mm = pair_op<32>(mm, OpMax{});
         const float c = mm == -__builtin_inff() ? 0.f : fast_exp2(m[h] - mm);
         l[h] *= c;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] *= c;
         m[h] = mm;
+        if constexpr (LPR <= 8) {
+            l[h] = pair_op<8>(l[h], OpAdd{});
 #pragma unroll
-        for (int off = LPR; off < kWave; off <<= 1) {
-            l[h] += __shfl_xor(l[h], off);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+            for (int e = 0; e < EPL; ++e) acc[h][e] = pair_op<8>(acc[h][e], OpAdd{});
         }
+        if constexpr (LPR <= 16) {
+            l[h] = pair_op<16>(l[h], OpAdd{});
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] = pair_op<16>(acc[h][e], OpAdd{});
+        }
+        l[h] = pair_op<32>(l[h], OpAdd{});
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = pair_op<32>(acc[h][e], OpAdd{});
     }
     if (lane < LPR) {
 #pragma unroll

@@ -48,8 +48,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const int kvh = (g / gpk) % Hkv;
     const int h0 = kvh * G + (gpk == 1 ? 0 : g % gpk);
     // every load is issued before any result is waited for: the query chunk, the
-    // first centroid chunk, the size and the community count (the workgroup runs
-    // even past the graph's count, so that no load waits behind a branch)
+    // first centroid chunk, the size and the community count
     using Q4 = typename std::conditional<sizeof(T) == 2, uint2, float4>::type;
     Q4 qraw[NQ];
 #pragma unroll
@@ -64,6 +63,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     for (int k = 0; k < KC; ++k) cur[k] = cp[(size_t)k * Cmax];
     const int sz = comm_size[(size_t)g * Cmax + c];
     const int C = min(num_comms[g], Cmax);
+    // a workgroup wholly past the graph's count leaves now: only its first chunk
+    // (issued before the count was known) was fetched in vain
+    if ((int)(blockIdx.x * kScoreThreads) >= C) return;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
         float e4[4];
