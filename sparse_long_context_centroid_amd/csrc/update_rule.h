@@ -19,14 +19,24 @@
 
 namespace ckv {
 
-// LDS floats one updating wavefront needs: k_new widened to fp64.
-constexpr int kUpdLdsFloats(int D) { return 2 * D; }
+// Lanes per candidate slot: the wave's 64 lanes cover CKV_MAX_CAND slots.
+constexpr int kUpdLanesPerCand = kWave / CKV_MAX_CAND;
+// Row stride (floats) of a candidate centroid parked in LDS: padded by one float4
+// so that the candidate lanes' element-order reads fall in different banks.
+constexpr int kUpdCentStride(int D) { return D + 4; }
+// LDS floats one updating wavefront needs: k_new widened to fp64, then the
+// candidates' centroids.
+constexpr int kUpdLdsFloats(int D) { return 2 * D + CKV_MAX_CAND * kUpdCentStride(D); }
 
 // One wavefront updates graph g.  cand[0..M) are community ids (-1 = none);
 // C communities are in use.  lds_row holds kUpdLdsFloats(D) floats of LDS private
-// to this wave (k_new widened to fp64).
-// When write_kv, the wave also stores k_new / v_new into K/V row `kv_row`
-// (element offset), or flags an unmapped page.
+// to this wave.  When write_kv, the wave also stores k_new / v_new into K/V row
+// `kv_row` (element offset), or flags an unmapped page.
+//
+// Every global read is issued before any is waited for, in two dependent rounds:
+// the candidate ids, then all candidates' centroids (4 lanes per candidate) with
+// their sizes, capacities and starts.  The centroids are parked in LDS; the lane
+// that owns a candidate then sums its distance there, in element order.
 template <typename T, int D>
 __device__ __forceinline__ void local_update_wave(const T *__restrict__ kn, const T *__restrict__ vn,
                                   const int *cand, int M, int C, size_t g, int Cmax,
@@ -38,51 +48,55 @@ __device__ __forceinline__ void local_update_wave(const T *__restrict__ kn, cons
                                   bool kv_ok, int32_t *__restrict__ assigned,
                                   int32_t *__restrict__ err, float *lds_row) {
 #pragma clang fp contract(off)
+    constexpr int LPC = kUpdLanesPerCand;
+    constexpr int CS = kUpdCentStride(D);
+    constexpr int KPL = D / 4 / LPC;  // float4 chunks of a centroid per lane
+    static_assert((D / 4) % LPC == 0, "whole chunks per lane");
     const int lane = threadIdx.x & (kWave - 1);
-    // k_new widened to fp64 once, into LDS, so the candidate lanes read it there
-    // instead of issuing one dependent scalar load per element
+    const int slot = lane / LPC, part = lane % LPC;
     double *kn64 = reinterpret_cast<double *>(lds_row);
-    for (int i = lane; i < D; i += kWave) kn64[i] = (double)to_f32(kn[i]);
+    float *lc = lds_row + 2 * D;
+    // round 1: this lane's candidate id and its share of k_new
+    const int cc = cand[min(slot, M - 1)];
+    T knr[D / kWave > 0 ? D / kWave : 1];
+#pragma unroll
+    for (int r = 0; r < D / kWave; ++r) knr[r] = kn[lane + r * kWave];
+    const int c = (slot < M && cc >= 0 && cc < C) ? cc : -1;
+    const int cl = c >= 0 ? c : 0;  // loads below are unconditional
+    // round 2: the centroid share, size, capacity and start of the candidate
+    const float4 *cp = reinterpret_cast<const float4 *>(cent) + g * (D / 4) * Cmax + cl;
+    float4 v[KPL];
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) v[k] = cp[(size_t)(part + k * LPC) * Cmax];
+    int sz = comm_size[g * Cmax + cl];
+    const int cap = comm_cap[g * Cmax + cl];
+    const int st = comm_start[g * Cmax + cl];
+#pragma unroll
+    for (int r = 0; r < D / kWave; ++r) kn64[lane + r * kWave] = (double)to_f32(knr[r]);
+#pragma unroll
+    for (int k = 0; k < KPL; ++k)
+        *reinterpret_cast<float4 *>(lc + slot * CS + (part + k * LPC) * 4) = v[k];
     __builtin_amdgcn_wave_barrier();
-    // lane m < M owns candidate m: its size, capacity and start are fetched with
-    // the first chunk of its centroid; the centroid streams through registers in
-    // chunks of 8 float4 (the distance stays an element-order sum)
-    int c = -1;
-    if (lane < M) {
-        const int cc = cand[lane];
-        if (cc >= 0 && cc < C) c = cc;
-    }
-    int sz = 0, cap = 0, st = 0;
+    // the first lane of each candidate slot sums the distance in element order
     double dist = __builtin_inf();
-    if (c >= 0) {
-        const float4 *cp = reinterpret_cast<const float4 *>(cent) + g * (D / 4) * Cmax + c;
-        sz = comm_size[g * Cmax + c];
-        cap = comm_cap[g * Cmax + c];
-        st = comm_start[g * Cmax + c];
+    if (part == 0 && c >= 0) {
         double s = 0.0;
-#pragma unroll 1
-        for (int k0 = 0; k0 < D / 4; k0 += 8) {
-            float4 v[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = cp[(size_t)(k0 + k) * Cmax];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float m4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const double diff = kn64[(k0 + k) * 4 + e] - (double)m4[e];
-                    const double sq = diff * diff;
-                    s = s + sq;
-                }
-            }
+        const float *mu = lc + slot * CS;
+#pragma unroll 8
+        for (int i = 0; i < D; ++i) {
+            const double diff = kn64[i] - (double)mu[i];
+            const double sq = diff * diff;
+            s = s + sq;
         }
         dist = s;
     }
-    // argmin over (distance, id) across the wave
-    int best = c;
+    // argmin over (distance, id) among the slot-owning lanes (lanes 0, LPC, 2*LPC,
+    // ...: a butterfly over distances LPC..32 stays inside that set), then made
+    // wave-uniform from lane 0
+    int best = part == 0 ? c : -1;
     double bd = dist;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
+    for (int off = LPC; off < kWave; off <<= 1) {
         const double od = __shfl_xor(bd, off);
         const int oc = __shfl_xor(best, off);
         if (oc >= 0 && (best < 0 || od < bd || (od == bd && oc < best))) {
@@ -90,33 +104,35 @@ __device__ __forceinline__ void local_update_wave(const T *__restrict__ kn, cons
             best = oc;
         }
     }
-    const unsigned long long win = __ballot(c >= 0 && c == best);
-    int slot = -1;
+    best = __shfl(best, 0);
+    const unsigned long long win = __ballot(part == 0 && c >= 0 && c == best);
+    int slot_new = -1;
     int wl = 0;
     if (win) {
         wl = __ffsll((long long)win) - 1;
-        sz = __shfl(sz, wl);
-        cap = __shfl(cap, wl);
-        st = __shfl(st, wl);
-        __builtin_amdgcn_wave_barrier();
-        if (sz < cap) {
-            slot = sz;
+        const int wsz = __shfl(sz, wl);
+        const int wcap = __shfl(cap, wl);
+        const int wst = __shfl(st, wl);
+        if (wsz < wcap) {
+            slot_new = wsz;
             if (lane == 0) {
-                members[(size_t)st + sz] = n;
-                comm_size[g * Cmax + best] = sz + 1;
+                members[(size_t)wst + wsz] = n;
+                comm_size[g * Cmax + best] = wsz + 1;
             }
         } else if (lane == 0) {
             set_err(err, CKV_DEVERR_CAPACITY);
         }
     }
-    if (lane == 0) assigned[g] = slot >= 0 ? best : -1;
-    if (slot >= 0) {
-        const double cnt = (double)(slot + 1);
-        float *mu = cent + g * (D / 4) * Cmax * 4;
+    if (lane == 0) assigned[g] = slot_new >= 0 ? best : -1;
+    if (slot_new >= 0) {
+        // running mean of the winner, from its LDS copy
+        const double cnt = (double)(slot_new + 1);
+        const float *mu = lc + (wl / LPC) * CS;
+        float *out = cent + g * (D / 4) * Cmax * 4;
         for (int i = lane; i < D; i += kWave) {
-            const double m0 = (double)mu[((size_t)(i / 4) * Cmax + best) * 4 + i % 4];
+            const double m0 = (double)mu[i];
             const double step = (kn64[i] - m0) / cnt;
-            mu[((size_t)(i / 4) * Cmax + best) * 4 + i % 4] = (float)(m0 + step);
+            out[((size_t)(i / 4) * Cmax + best) * 4 + i % 4] = (float)(m0 + step);
         }
     }
     if (write_kv) {
