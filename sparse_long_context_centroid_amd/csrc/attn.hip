@@ -414,10 +414,20 @@ __device__ __forceinline__ void merge_graph(int g, int Hq, int Hkv, int gpk,
     // weights: one wave per head
     for (int hh = w; hh < GH; hh += blockDim.x / kWave) {
         const float *ph = pbase + (size_t)hh * max_splits * (D + 2);
+        if (max_splits <= kWave) {
+            // one split per lane: (m, l) fetched once, reduced with DPP
+            float2 ml = make_float2(-__builtin_inff(), 0.f);
+            if (lane < max_splits) ml = *reinterpret_cast<const float2 *>(ph + (size_t)lane * (D + 2));
+            const float mm = wave_max_f(ml.x);
+            const float f = ml.x == -__builtin_inff() ? 0.f : fast_exp2(ml.x - mm);
+            const float ll = wave_sum_f(ml.y * f);
+            const float inv = ll > 0.f ? 1.f / ll : 0.f;
+            if (lane < max_splits) s_w[hh * max_splits + lane] = f * inv;
+            continue;
+        }
         float mm = -__builtin_inff();
         for (int s = lane; s < max_splits; s += kWave) mm = fmaxf(mm, ph[(size_t)s * (D + 2)]);
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
+        mm = wave_max_f(mm);
         float ll = 0.f;
         for (int s = lane; s < max_splits; s += kWave) {
             const float ms = ph[(size_t)s * (D + 2)];
@@ -425,8 +435,7 @@ __device__ __forceinline__ void merge_graph(int g, int Hq, int Hkv, int gpk,
             s_w[hh * max_splits + s] = f;
             ll += ph[(size_t)s * (D + 2) + 1] * f;
         }
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) ll += __shfl_xor(ll, off);
+        ll = wave_sum_f(ll);
         const float inv = ll > 0.f ? 1.f / ll : 0.f;
         for (int s = lane; s < max_splits; s += kWave) s_w[hh * max_splits + s] *= inv;
     }

@@ -50,6 +50,45 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// DPP move of a float inside 16-lane rows (lanes without a source keep their own
+// value), used by the wave reductions below.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_keep(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL,
+                                                      ROW_MASK, 0xF, false));
+}
+
+// Reductions of a float over the wavefront, as wave-uniform values: row shifts
+// 1, 2, 4, 8, then the row totals carried by row_bcast 15 / 31 into the last row.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce_f(float x, Op op) {
+    x = op(x, dpp_keep<0x111>(x));       // row_shr:1
+    x = op(x, dpp_keep<0x112>(x));       // row_shr:2
+    x = op(x, dpp_keep<0x114>(x));       // row_shr:4
+    x = op(x, dpp_keep<0x118>(x));       // row_shr:8
+    x = op(x, dpp_keep<0x142, 0xA>(x));  // row_bcast:15
+    x = op(x, dpp_keep<0x143, 0xC>(x));  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
+}
+__device__ __forceinline__ float wave_max_f(float x) {
+    return wave_reduce_f(x, [](float a, float b) { return fmaxf(a, b); });
+}
+// Sum: here lanes without a DPP source must contribute 0, not their own value.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_zero(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, true));
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+    x += dpp_zero<0x111>(x);
+    x += dpp_zero<0x112>(x);
+    x += dpp_zero<0x114>(x);
+    x += dpp_zero<0x118>(x);
+    x += dpp_zero<0x142, 0xA>(x);
+    x += dpp_zero<0x143, 0xC>(x);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
+}
+
 // Order-preserving map of an fp32 score to u32 (larger score -> larger key);
 // -0 and +0 compare equal as floats, so both map to the key of +0.
 __device__ __forceinline__ uint32_t order_key(float s) {

@@ -80,30 +80,12 @@ __device__ __forceinline__ void block_sums(int (&v)[N], int *buf) {
     }
 }
 
-// Maximum of a float over the wavefront, as a wave-uniform value: DPP row shifts
-// (lanes without a source keep their own value), then the row totals carried by
-// row_bcast 15 / 31 into the last row.
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ float dpp_keep(float x) {
-    return __int_as_float(
-        __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
-}
-__device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, dpp_keep<0x111>(x));       // row_shr:1
-    x = fmaxf(x, dpp_keep<0x112>(x));       // row_shr:2
-    x = fmaxf(x, dpp_keep<0x114>(x));       // row_shr:4
-    x = fmaxf(x, dpp_keep<0x118>(x));       // row_shr:8
-    x = fmaxf(x, dpp_keep<0x142, 0xA>(x));  // row_bcast:15
-    x = fmaxf(x, dpp_keep<0x143, 0xC>(x));  // row_bcast:31
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
-}
-
 // Block maxima of two floats (all threads get both); `buf` holds 2*kSelWaves.
 __device__ __forceinline__ void block_max2(float (&v)[2], float *buf) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) v[j] = wave_max(v[j]);
+    for (int j = 0; j < 2; ++j) v[j] = wave_max_f(v[j]);
     if (lane == 0) {
         buf[w] = v[0];
         buf[kSelWaves + w] = v[1];
