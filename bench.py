@@ -118,6 +118,33 @@ class Timed:
         return [self.ev[2 * i].elapsed_time(self.ev[2 * i + 1]) for i in range(4)]
 
 
+def dense_baseline(layers, qkv, wl, scrub, args, elem):
+    """The same layers through ckv_dense_decode_attn (attention over every cached
+    token, no selection), same cold protocol, on the state the sparse steps left."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    outs = [torch.empty_like(l.out) for l in layers]
+    T = args.warmup + args.steps
+    ms = []
+    for t in range(min(args.steps, 10) + 2):
+        tot = 0.0
+        for lay, (q, _, _), o in zip(layers, qkv, outs):
+            if not args.warm:
+                scrub_sum = scrub.sum()
+            ev[0].record()
+            lay.dense(q[T - 1], wl.scale, out=o)
+            ev[1].record()
+            torch.cuda.synchronize()
+            tot += ev[0].elapsed_time(ev[1])
+        if t >= 2:
+            ms.append(tot)
+    n = np.concatenate([l.seq_len.cpu().numpy() for l in layers]).astype(np.float64)
+    kv_bytes = float(n.sum()) * layers[0].Hkv * 2 * layers[0].d * elem
+    step_ms = float(np.mean(ms))
+    return dict(ms_per_step=step_ms, tokens_per_s=wl.B / (step_ms / 1e3),
+                kv_bytes_per_step=kv_bytes, gbs=kv_bytes / (step_ms / 1e3) / 1e9,
+                steps=len(ms))
+
+
 def build_layers(wl, index_stride):
     layers = []
     for li in range(len(wl.layers)):
@@ -161,6 +188,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--scrub-mib", type=int, default=1024)
     ap.add_argument("--warm", action="store_true", help="no cache scrub between steps")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense-attention baseline (every cached token)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before timing, run a plain device copy of this many MiB three times "
@@ -236,6 +265,9 @@ def main():
         if t == 0 or (t + 1) % 10 == 0:
             log(f"[bench] step {t + 1}/{T}")
     wall = time.perf_counter() - wall0
+    dense = None
+    if not args.no_dense:
+        dense = dense_baseline(layers, qkv, wl, scrub, args, elem)
     err = max(int(l.err.item()) for l in layers)
     if err:
         raise SystemExit(f"device error flag {err} during the benchmark")
@@ -290,6 +322,9 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if dense is not None:
+        dense["sparse_speedup"] = dense["ms_per_step"] / (total_ms / K)
+        res["dense_baseline"] = dense
     print(json.dumps(res), flush=True)
 
 

@@ -189,6 +189,25 @@ CKV_API ckv_status ckv_local_update(const ckv_dims *dims, const void *k_new, con
                             void *stream);
 
 /*
+ * Dense decode attention, the baseline the sparse path is measured against: for
+ * every query head h of sequence b, exact softmax attention over all cached tokens
+ * 0..seq_len[b]-1 of its KV head, read through the page table -- the same
+ * computation as ckv_sparse_decode_attn with a full index list [RIT-graph: the
+ * method keeps the whole cache and attends over chosen communities instead].
+ * dims.graphs_per_kv and max_comms are validated but play no part.
+ *   q    : [B][Hq][d] (dims.dtype);  out : [B][Hq][d] fp32
+ *   ws   : >= ckv_dense_workspace_size(dims, kv) bytes (split partials; pieces are
+ *          sized so that a KV head has at most 64 of them for the largest context
+ *          max_pages_per_seq * page_size)
+ * err_flag: CKV_DEVERR_UNMAPPED_PAGE for unmapped pages below seq_len (skipped).
+ * Returns 0 from the size query for invalid dims or kv.
+ */
+CKV_API size_t ckv_dense_workspace_size(const ckv_dims *dims, const ckv_kv *kv);
+CKV_API ckv_status ckv_dense_decode_attn(const ckv_dims *dims, const void *q, const ckv_kv *kv,
+                                         float scale, float *out, void *ws, size_t ws_bytes,
+                                         int32_t *err_flag, void *stream);
+
+/*
  * One whole decode step, the four operations above in 4 kernel launches:
  * scoring; selection + compaction; sparse attention (split partials) with the
  * local update running in extra workgroups of the same launch (attention reads

@@ -69,6 +69,8 @@ def load(path: str = LIB_PATH):
         "ckv_local_update": (i32, [pd, P, P, P, i32, pg, pk, P, P, P]),
         "ckv_decode_step": (i32, [pd, P, P, P, pg, pk, P, i32, C.c_float, P, P, i32, P, P, P,
                                   P, P, P, P, sz, P, P, P]),
+        "ckv_dense_workspace_size": (sz, [pd, pk]),
+        "ckv_dense_decode_attn": (i32, [pd, P, pk, C.c_float, P, P, sz, P, P]),
         "ckv_status_string": (C.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -81,7 +83,8 @@ def load(path: str = LIB_PATH):
 
 EXPORTED = ("ckv_workspace_size", "ckv_centroids_from_rows", "ckv_centroids_to_rows",
             "ckv_score_centroids", "ckv_select", "ckv_sparse_decode_attn", "ckv_local_update",
-            "ckv_decode_step", "ckv_status_string")
+            "ckv_decode_step", "ckv_dense_workspace_size", "ckv_dense_decode_attn",
+            "ckv_status_string")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -154,6 +157,16 @@ def ckv_sparse_decode_attn(dims, q, kv, index_list, index_len, scale, out, ws, e
                                          index_list.shape[1], _ptr(index_len), scale, _ptr(out),
                                          _ptr(ws), ws.numel() * ws.element_size(), _ptr(err_flag),
                                          _stream(stream)), "ckv_sparse_decode_attn")
+
+
+def ckv_dense_workspace_size(dims, kv) -> int:
+    return int(load().ckv_dense_workspace_size(C.byref(dims), C.byref(kv)))
+
+
+def ckv_dense_decode_attn(dims, q, kv, scale, out, ws, err_flag, stream=None):
+    _check(load().ckv_dense_decode_attn(C.byref(dims), _ptr(q), C.byref(kv), scale, _ptr(out),
+                                        _ptr(ws), ws.numel() * ws.element_size(), _ptr(err_flag),
+                                        _stream(stream)), "ckv_dense_decode_attn")
 
 
 def ckv_local_update(dims, k_new, v_new, cand, n_cand, graphs, kv, assigned, err_flag,
@@ -251,6 +264,16 @@ class DecodeLayer:
     def attend(self, q, scale):
         ckv_sparse_decode_attn(self.dims, q, self.kv, self.index_list, self.index_len, scale,
                                self.out, self.ws, self.err)
+
+    def dense(self, q, scale, out=None):
+        """Dense baseline: attention over every cached token (no selection)."""
+        if getattr(self, "dense_ws", None) is None:
+            n = ckv_dense_workspace_size(self.dims, self.kv)
+            if n == 0:
+                raise CkvError("invalid dims for the dense workspace")
+            self.dense_ws = torch.empty(n, dtype=torch.uint8, device=self.out.device)
+        out = self.out if out is None else out
+        ckv_dense_decode_attn(self.dims, q, self.kv, scale, out, self.dense_ws, self.err)
 
     def update(self, k_new, v_new):
         ckv_local_update(self.dims, k_new, v_new, self.cand, self.M, self.graphs, self.kv,

@@ -139,6 +139,28 @@ ckv_status ckv_sparse_decode_attn(const ckv_dims *dims, const void *q, const ckv
         ckv::launch_attn_merge(p, index_stride, out, static_cast<float *>(ws), nullptr, st));
 }
 
+size_t ckv_dense_workspace_size(const ckv_dims *dims, const ckv_kv *kv) {
+    Problem p;
+    if (make_problem(dims, p) != CKV_OK || check_kv(kv, p) != CKV_OK) return 0;
+    return ckv::dense_partial_floats(p, *kv) * sizeof(float);
+}
+
+ckv_status ckv_dense_decode_attn(const ckv_dims *dims, const void *q, const ckv_kv *kv,
+                                 float scale, float *out, void *ws, size_t ws_bytes,
+                                 int32_t *err_flag, void *stream) {
+    Problem p;
+    ckv_status s = make_problem(dims, p);
+    if (s != CKV_OK) return s;
+    if ((s = check_kv(kv, p)) != CKV_OK) return s;
+    if (!q || !out) return CKV_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < ckv_dense_workspace_size(dims, kv)) return CKV_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((s = hip_status(ckv::launch_dense_partials(p, q, *kv, scale, static_cast<float *>(ws),
+                                                   err_flag, st))) != CKV_OK)
+        return s;
+    return hip_status(ckv::launch_dense_merge(p, *kv, out, static_cast<float *>(ws), st));
+}
+
 ckv_status ckv_local_update(const ckv_dims *dims, const void *k_new, const void *v_new,
                             const int32_t *cand, int32_t n_cand, const ckv_graphs *graphs,
                             const ckv_kv *kv, int32_t *assigned, int32_t *err_flag,

@@ -140,13 +140,21 @@ struct UpdateArgs {
     int32_t *assigned;
 };
 
-template <typename T, int D, int GH, bool WITH_UPDATE>
+// What a launch of attn_kernel reads as its token list.
+enum AttnMode {
+    kAttnIndexed = 0,        // the index list of each graph
+    kAttnIndexedUpdate = 1,  // the same, plus the local update in grid row 0
+    kAttnDense = 2           // every cached token 0..seq_len-1 (the dense baseline)
+};
+
+template <typename T, int D, int GH, int MODE>
 __global__ __launch_bounds__(256) void attn_kernel(
     const T *__restrict__ q, T *__restrict__ kc, T *__restrict__ vc,
     const int32_t *__restrict__ page_table, int log2ps, int max_pages, int num_pages,
     int32_t *__restrict__ seq_len, const int32_t *__restrict__ idx, int idx_stride,
     const int32_t *__restrict__ idx_len, int Hq, int Hkv, int gpk, float scale_log2,
-    float *__restrict__ part, int max_splits, int32_t *__restrict__ err, UpdateArgs u) {
+    float *__restrict__ part, int max_splits, int chunks_per_wg, int32_t *__restrict__ err,
+    UpdateArgs u) {
     constexpr int EPL = 16 / sizeof(T);     // row elements per lane
     constexpr int LPR = D / EPL;            // lanes per row
     constexpr int RPW = kWave / LPR;        // rows per wave-wide load
@@ -164,7 +172,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
     __shared__ float s_l[kAttnWaves][GH];
     __shared__ float s_acc[kAttnWaves][GH][D];
 
-    if constexpr (WITH_UPDATE) {
+    if constexpr (MODE == kAttnIndexedUpdate) {
         // grid row 0: the local update, one wave per graph (dispatched first, so it
         // runs under the K/V stream of the attention workgroups); seq_len advances
         // in the merge launch
@@ -184,7 +192,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
     }
     const int NG = gridDim.x;
     const int g = graph_of_column(blockIdx.x, NG, gpk);
-    const int split = (int)blockIdx.y - (WITH_UPDATE ? 1 : 0);
+    const int split = (int)blockIdx.y - (MODE == kAttnIndexedUpdate ? 1 : 0);
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
@@ -192,8 +200,10 @@ __global__ __launch_bounds__(256) void attn_kernel(
     const int b = g / (Hkv * gpk);
     const int kvh = (g / gpk) % Hkv;
     const int h0 = kvh * G + (gpk == 1 ? 0 : g % gpk);
-    const int len = min(idx_len[g], idx_stride);
-    const int nsplit = (len + CH - 1) / CH;
+    const int n = seq_len[b];
+    const int len = MODE == kAttnDense ? n : min(idx_len[g], idx_stride);
+    const int span = CH * chunks_per_wg;  // tokens one workgroup may cover
+    const int nsplit = (len + span - 1) / span;
     if (split >= nsplit) {
         // an empty split still marks its partial (weight 0) so the merge can read
         // every split without knowing the list length
@@ -204,10 +214,9 @@ __global__ __launch_bounds__(256) void attn_kernel(
         }
         return;
     }
-    // balanced cut of the list into nsplit chunks
+    // balanced cut of the list into nsplit pieces of at most `span` tokens
     const int t_begin = (int)(((long long)len * split) / nsplit);
     const int t_end = (int)(((long long)len * (split + 1)) / nsplit);
-    const int n = seq_len[b];
     const int ls = lane % LPR;  // slice of the row this lane reads
     const int rs = lane / LPR;  // row slot inside a wave-wide load
 
@@ -226,12 +235,24 @@ __global__ __launch_bounds__(256) void attn_kernel(
         }
     }
 
+    // running (m, l, acc) of this lane's row slot, over all chunks of the piece
+    float m[GH], l[GH], acc[GH][EPL];
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+        m[h] = -__builtin_inff();
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    }
+    // one chunk of at most CH tokens [c0, c_end): rows to LDS, then the K/V rows of
+    // this lane's slots, folded into (m, l, acc)
+    auto chunk = [&](const int c0, const int c_end) {
     // ---- phase A: list entries -> row indices in LDS
     for (int t = tid; t < CH; t += blockDim.x) {
-        const int te = t_begin + t;
+        const int te = c0 + t;
         int row = -1;
-        if (te < t_end) {
-            const int pos = idx[(size_t)g * idx_stride + te];
+        if (te < c_end) {
+            const int pos = MODE == kAttnDense ? te : idx[(size_t)g * idx_stride + te];
             if (pos >= 0 && pos < n) {
                 const int lp = pos >> log2ps;
                 const int pg = lp < max_pages ? page_table[(size_t)b * max_pages + lp] : -1;
@@ -278,14 +299,6 @@ __global__ __launch_bounds__(256) void attn_kernel(
     __builtin_amdgcn_sched_barrier(0);
 
     // online softmax over batches of kSub loads; m, l, acc are per row slot
-    float m[GH], l[GH], acc[GH][EPL];
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-        m[h] = -__builtin_inff();
-        l[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-    }
 #pragma unroll
     for (int i0 = 0; i0 < NLD; i0 += kSub) {
         float z[kSub][GH];
@@ -322,6 +335,15 @@ __global__ __launch_bounds__(256) void attn_kernel(
                 for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
             }
         }
+    }
+    };
+    if constexpr (MODE == kAttnDense) {
+        for (int c0 = t_begin; c0 < t_end; c0 += CH) {
+            if (c0 != t_begin) __syncthreads();  // every wave has read s_row
+            chunk(c0, min(c0 + CH, t_end));
+        }
+    } else {
+        chunk(t_begin, t_end);  // an indexed piece is one chunk
     }
     // merge the RPW row slots of the wave (same dims, disjoint tokens, own maxima);
     // lanes L and L^off pair up with VALU lane swaps, no LDS round trips
@@ -473,40 +495,38 @@ __global__ __launch_bounds__(512) void merge_kernel(int Hq, int Hkv, int gpk,
     merge_graph<D, GH>(blockIdx.x, Hq, Hkv, gpk, out, part, max_splits, s_w);
 }
 
-template <typename T, int D, int GH, bool UPD>
+template <typename T, int D, int GH, int MODE>
 static void launch_partials_t(const Problem &p, const void *q, const ckv_kv &kv,
                               const int32_t *idx, int idx_stride, const int32_t *idx_len,
                               float scale, float *partials, int32_t *err, const UpdateArgs &u,
-                              hipStream_t st) {
-    const int ms = attn_max_splits(p, idx_stride);
-    hipExtLaunchKernelGGL((attn_kernel<T, D, GH, UPD>), dim3(p.NG(), ms + (UPD ? 1 : 0)),
-                          dim3(256), 0, st, p.ev_start, p.ev_stop, 0,
-                          static_cast<const T *>(q), static_cast<T *>(kv.k),
-                       static_cast<T *>(kv.v), kv.page_table, log2_pow2(kv.page_size),
-                       kv.max_pages_per_seq, kv.num_pages, kv.seq_len, idx, idx_stride, idx_len,
-                       p.Hq, p.Hkv, p.gpk, scale * kLog2e, partials, ms, err, u);
+                              int ms, int cpw, hipStream_t st) {
+    hipExtLaunchKernelGGL((attn_kernel<T, D, GH, MODE>),
+                          dim3(p.NG(), ms + (MODE == kAttnIndexedUpdate ? 1 : 0)), dim3(256), 0,
+                          st, p.ev_start, p.ev_stop, 0, static_cast<const T *>(q),
+                          static_cast<T *>(kv.k), static_cast<T *>(kv.v), kv.page_table,
+                          log2_pow2(kv.page_size), kv.max_pages_per_seq, kv.num_pages,
+                          kv.seq_len, idx, idx_stride, idx_len, p.Hq, p.Hkv, p.gpk,
+                          scale * kLog2e, partials, ms, cpw, err, u);
 }
 
-hipError_t launch_attn_partials(const Problem &p, const void *q, const ckv_kv &kv,
-                                const int32_t *idx, int idx_stride, const int32_t *idx_len,
-                                float scale, float *partials, int32_t *err, const UpdateSpec *upd,
-                                hipStream_t st) {
+// One launcher for the three modes; GH = heads per graph of `p`.
+static hipError_t launch_mode(const Problem &p, int mode, const void *q, const ckv_kv &kv,
+                              const int32_t *idx, int idx_stride, const int32_t *idx_len,
+                              float scale, float *partials, int32_t *err, const UpdateArgs &u,
+                              int ms, int cpw, hipStream_t st) {
     const int GH = p.heads_per_graph();
-    UpdateArgs u{};
-    if (upd) {
-        u = UpdateArgs{upd->k_new, upd->v_new, upd->cand, upd->n_cand, upd->graphs->centroids,
-                       upd->graphs->num_comms, upd->graphs->comm_start, upd->graphs->comm_size,
-                       upd->graphs->comm_cap, upd->graphs->members, p.Cmax, p.NG(),
-                       upd->assigned};
-    }
 #define CKV_ATTN_CASE(TT, DT, DD, HH)                                                          \
     if (p.dtype == DT && p.D == DD && GH == HH) {                                              \
-        if (upd)                                                                               \
-            launch_partials_t<TT, DD, HH, true>(p, q, kv, idx, idx_stride, idx_len, scale,     \
-                                                partials, err, u, st);                         \
+        if (mode == kAttnIndexedUpdate)                                                        \
+            launch_partials_t<TT, DD, HH, kAttnIndexedUpdate>(p, q, kv, idx, idx_stride,       \
+                                                              idx_len, scale, partials, err,   \
+                                                              u, ms, cpw, st);                 \
+        else if (mode == kAttnDense)                                                           \
+            launch_partials_t<TT, DD, HH, kAttnDense>(p, q, kv, idx, idx_stride, idx_len,      \
+                                                      scale, partials, err, u, ms, cpw, st);   \
         else                                                                                   \
-            launch_partials_t<TT, DD, HH, false>(p, q, kv, idx, idx_stride, idx_len, scale,    \
-                                                 partials, err, u, st);                        \
+            launch_partials_t<TT, DD, HH, kAttnIndexed>(p, q, kv, idx, idx_stride, idx_len,    \
+                                                        scale, partials, err, u, ms, cpw, st); \
         return hipGetLastError();                                                              \
     }
     CKV_ATTN_CASE(bf16_t, CKV_DT_BF16, 128, 1) CKV_ATTN_CASE(bf16_t, CKV_DT_BF16, 128, 2)
@@ -521,22 +541,56 @@ hipError_t launch_attn_partials(const Problem &p, const void *q, const ckv_kv &k
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_merge(const Problem &p, int idx_stride, float *out, const float *partials,
-                             int32_t *bump_seq_len, hipStream_t st) {
+hipError_t launch_attn_partials(const Problem &p, const void *q, const ckv_kv &kv,
+                                const int32_t *idx, int idx_stride, const int32_t *idx_len,
+                                float scale, float *partials, int32_t *err, const UpdateSpec *upd,
+                                hipStream_t st) {
+    UpdateArgs u{};
+    if (upd) {
+        u = UpdateArgs{upd->k_new, upd->v_new, upd->cand, upd->n_cand, upd->graphs->centroids,
+                       upd->graphs->num_comms, upd->graphs->comm_start, upd->graphs->comm_size,
+                       upd->graphs->comm_cap, upd->graphs->members, p.Cmax, p.NG(),
+                       upd->assigned};
+    }
+    return launch_mode(p, upd ? kAttnIndexedUpdate : kAttnIndexed, q, kv, idx, idx_stride,
+                       idx_len, scale, partials, err, u, attn_max_splits(p, idx_stride), 1, st);
+}
+
+hipError_t launch_dense_partials(const Problem &p, const void *q, const ckv_kv &kv, float scale,
+                                 float *partials, int32_t *err, hipStream_t st) {
+    const Problem pd = dense_problem(p);
+    int cpw = 1;
+    const int ms = dense_max_splits(pd, kv, &cpw);
+    return launch_mode(pd, kAttnDense, q, kv, nullptr, 0, nullptr, scale, partials, err,
+                       UpdateArgs{}, ms, cpw, st);
+}
+
+static hipError_t launch_merge(const Problem &p, int ms, float *out, const float *partials,
+                               int32_t *bump_seq_len, hipStream_t st) {
     const int GH = p.heads_per_graph();
-    const int ms = attn_max_splits(p, idx_stride);
 #define CKV_MERGE_CASE(DD, HH)                                                                 \
     if (p.D == DD && GH == HH) {                                                               \
         hipExtLaunchKernelGGL((merge_kernel<DD, HH>), dim3(p.NG()), dim3(512),                 \
                               (size_t)HH * ms * sizeof(float), st, p.ev_start, p.ev_stop, 0,   \
-                              p.Hq, p.Hkv, p.gpk, out,                                         \
-                           partials, ms, bump_seq_len);                                        \
+                              p.Hq, p.Hkv, p.gpk, out, partials, ms, bump_seq_len);            \
         return hipGetLastError();                                                              \
     }
     CKV_MERGE_CASE(128, 1) CKV_MERGE_CASE(128, 2) CKV_MERGE_CASE(128, 4) CKV_MERGE_CASE(128, 8)
     CKV_MERGE_CASE(64, 1) CKV_MERGE_CASE(64, 2) CKV_MERGE_CASE(64, 4) CKV_MERGE_CASE(64, 8)
 #undef CKV_MERGE_CASE
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_merge(const Problem &p, int idx_stride, float *out, const float *partials,
+                             int32_t *bump_seq_len, hipStream_t st) {
+    return launch_merge(p, attn_max_splits(p, idx_stride), out, partials, bump_seq_len, st);
+}
+
+hipError_t launch_dense_merge(const Problem &p, const ckv_kv &kv, float *out,
+                              const float *partials, hipStream_t st) {
+    const Problem pd = dense_problem(p);
+    int cpw = 1;
+    return launch_merge(pd, dense_max_splits(pd, kv, &cpw), out, partials, nullptr, st);
 }
 
 }  // namespace ckv

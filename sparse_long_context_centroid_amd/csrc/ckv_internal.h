@@ -42,6 +42,29 @@ inline int log2_pow2(int x) {
     return l;
 }
 
+// Dense baseline: one graph per KV head holding its G query heads (every cached
+// token is read, so no graph structure applies).  A workgroup covers cpw chunks
+// so that a graph has at most 64 pieces (one merge load round).
+inline Problem dense_problem(const Problem &p) {
+    Problem d = p;
+    d.gpk = 1;
+    return d;
+}
+inline int dense_max_splits(const Problem &p, const ckv_kv &kv, int *cpw) {
+    const int ch = attn_chunk(p.D, p.elem_bytes());
+    const long long max_ctx = (long long)kv.max_pages_per_seq * kv.page_size;
+    const long long c = (max_ctx + (long long)ch * 64 - 1) / ((long long)ch * 64);
+    *cpw = c < 1 ? 1 : (int)c;
+    const long long span = (long long)ch * *cpw;
+    const long long ms = (max_ctx + span - 1) / span;
+    return ms < 1 ? 1 : (int)ms;
+}
+inline size_t dense_partial_floats(const Problem &p, const ckv_kv &kv) {
+    const Problem d = dense_problem(p);
+    int cpw;
+    return (size_t)d.NG() * d.heads_per_graph() * dense_max_splits(d, kv, &cpw) * (d.D + 2);
+}
+
 // Workspace of the attention call: partials NG * GH * max_splits * (D + 2) fp32.
 inline size_t attn_partial_floats(const Problem &p, int index_stride) {
     return (size_t)p.NG() * p.heads_per_graph() * attn_max_splits(p, index_stride) * (p.D + 2);
@@ -71,6 +94,11 @@ hipError_t launch_attn_partials(const Problem &p, const void *q, const ckv_kv &k
                                 hipStream_t st);
 hipError_t launch_attn_merge(const Problem &p, int idx_stride, float *out, const float *partials,
                              int32_t *bump_seq_len, hipStream_t st);
+// Dense baseline: attention over every cached token of each sequence.
+hipError_t launch_dense_partials(const Problem &p, const void *q, const ckv_kv &kv, float scale,
+                                 float *partials, int32_t *err, hipStream_t st);
+hipError_t launch_dense_merge(const Problem &p, const ckv_kv &kv, float *out,
+                              const float *partials, hipStream_t st);
 hipError_t launch_update(const Problem &p, const void *k_new, const void *v_new,
                          const int32_t *cand, int n_cand, const ckv_graphs &gr, const ckv_kv &kv,
                          int32_t *assigned, int32_t *err, hipStream_t st);

@@ -101,6 +101,22 @@ def test_null_pointers_and_small_workspace(lib):
                                1 << 30, fake, None, None) == -1
 
 
+def test_dense_entry_points_validate(lib):
+    d = dims(B=4)
+    fake = C.c_void_p(0x1000)
+    kv = Bd.ckv_kv(fake, fake, fake, 16, 8208, 8208 * 4, fake)
+    # 32 KV heads x 4 query heads, pieces of 11 chunks of 192 tokens -> 63 pieces
+    assert lib.ckv_dense_workspace_size(C.byref(d), C.byref(kv)) == 32 * 4 * 63 * 130 * 4
+    assert lib.ckv_dense_workspace_size(C.byref(d), None) == 0
+    assert lib.ckv_dense_decode_attn(C.byref(d), None, C.byref(kv), 0.1, fake, fake, 1 << 30,
+                                     fake, None) == -1
+    assert lib.ckv_dense_decode_attn(C.byref(d), fake, C.byref(kv), 0.1, fake, fake, 64,
+                                     fake, None) == -3
+    kv_bad = Bd.ckv_kv(fake, fake, fake, 12, 8, 8, fake)
+    assert lib.ckv_dense_decode_attn(C.byref(d), fake, C.byref(kv_bad), 0.1, fake, fake,
+                                     1 << 30, fake, None) == -1
+
+
 def test_status_strings(lib):
     for s, txt in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported configuration"),
                    (-3, "workspace missing or too small"), (-4, "HIP launch failed")]:

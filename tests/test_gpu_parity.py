@@ -157,3 +157,39 @@ def test_parity_full_size_ragged_paged_deep_layer():
     _case("full size cfg4, layer 7 of 8")
     wl = I.make_workload(4, device="cuda", steps=2, layers=8)
     run_parity(wl, li=7, fused=True)
+
+
+@pytest.mark.parametrize("cfg,kw,sample", [
+    (0, dict(steps=1), None),
+    (1, dict(context=6000, steps=1), None),
+    (4, dict(contexts=[8192, 3000, 12345, 700], steps=1, layers=1), None),
+    (3, dict(steps=1), 12),
+])
+def test_dense_baseline_matches_oracle(cfg, kw, sample):
+    """The dense baseline (every cached token, through the page table) against the
+    oracle's attention over the full list 0..n-1; `sample` checks that many
+    (sequence, head) pairs of a full-size case."""
+    import oracle.ckv_oracle as O
+    _case(f"dense cfg{cfg} {kw}")
+    wl = I.make_workload(cfg, device="cuda", **kw)
+    layer = Bd.decode_layer_from_workload(wl, 0)
+    L = wl.layers[0]
+    q = L.q[0].contiguous()
+    layer.dense(q, wl.scale)
+    torch.cuda.synchronize()
+    assert int(layer.err.item()) == 0
+    out = layer.out.cpu().numpy().astype(np.float64)
+    K, V = H.logical_kv(wl, L)
+    qn = H.raw_np(q)
+    G = wl.Hq // wl.Hkv
+    pairs = [(b, h) for b in range(wl.B) for h in range(wl.Hq)]
+    if sample:
+        rng = np.random.default_rng(5)
+        pairs = [pairs[i] for i in rng.choice(len(pairs), sample, replace=False)]
+    for b, h in pairs:
+        n = int(wl.seq_len0[b])
+        ref = O.attend(qn[b, h], K[b, h // G], V[b, h // G], np.arange(n, dtype=np.int32),
+                       wl.scale)
+        err = np.abs(out[b, h] - ref)
+        rel = np.linalg.norm(out[b, h] - ref) / max(np.linalg.norm(ref), 1e-30)
+        assert err.max() <= 2e-3 and rel <= 1e-3, (b, h, err.max(), rel)
