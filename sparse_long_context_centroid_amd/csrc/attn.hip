@@ -287,12 +287,10 @@ __global__ __launch_bounds__(256) void attn_kernel(
     uint4 kr[NLD], vr[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i)
-        kr[i] = *reinterpret_cast<const uint4 *>(kc + (size_t)(rows[i] < 0 ? 0 : rows[i]) * D +
-                                                 ls * EPL);
+        kr[i] = load_nt(kc + (size_t)(rows[i] < 0 ? 0 : rows[i]) * D + ls * EPL);
 #pragma unroll
     for (int i = 0; i < NLD; ++i)
-        vr[i] = *reinterpret_cast<const uint4 *>(vc + (size_t)(rows[i] < 0 ? 0 : rows[i]) * D +
-                                                 ls * EPL);
+        vr[i] = load_nt(vc + (size_t)(rows[i] < 0 ? 0 : rows[i]) * D + ls * EPL);
     // all 2*NLD row loads stay in flight together: without this fence the
     // scheduler sinks most of them below the first softmax batch, which splits
     // the gather into dependent round trips

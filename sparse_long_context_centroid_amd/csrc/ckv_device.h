@@ -50,6 +50,19 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte load with the nontemporal hint, for data read once per step (the
+// selected K/V rows, the centroid stream): it is not kept in the caches.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const void *p) {
+    const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ float4 load_nt_f4(const void *p) {
+    const uint4 u = load_nt(p);
+    return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                       __uint_as_float(u.w));
+}
+
 // DPP move of a float inside 16-lane rows (lanes without a source keep their own
 // value), used by the wave reductions below.
 template <int CTRL, int ROW_MASK = 0xF>
