@@ -248,3 +248,51 @@ int ckvo_update(int d, const void *k_new, int dtype, const int32_t *cand, int n_
         *madds = ops;
     return best;
 }
+
+/*
+ * Centroid of every community recomputed from its member list: the plain mean of
+ * the member keys [RIT-graph: each community has a centre; RIT-plan: local
+ * assignments drift over long generations, and the partition is refreshed from
+ * time to time].  Reading: mu_c[i] = fp32( (sum over members j of K[j][i], in
+ * stored member order, fp64) / size_c ); empty communities get 0.
+ *
+ *   K       : key rows of one KV head, row j at K + j*d (dtype)
+ *   members : the pool; community c holds members[start[c] .. start[c]+size[c])
+ *   out     : C rows of d fp32
+ */
+void ckvo_rebuild(int d, const void *K, int dtype, const int32_t *members,
+                  const int32_t *start, const int32_t *size, int C, float *out)
+{
+    for (int c = 0; c < C; ++c) {
+        for (int i = 0; i < d; ++i) {
+            double s = 0.0;
+            for (int m = 0; m < size[c]; ++m)
+                s = s + widen(K, (long)members[start[c] + m] * d + i, dtype);
+            out[(long)c * d + i] = size[c] > 0 ? (float)(s / (double)size[c]) : 0.0f;
+        }
+    }
+}
+
+/*
+ * Drift of running-mean centroids from reference ones (e.g. rebuilt): the largest,
+ * over the non-empty communities, of ||mu_c - ref_c||_2 / ||ref_c||_2 (fp64;
+ * a zero reference row counts its absolute distance).  0 when none is non-empty.
+ */
+double ckvo_drift(int d, const float *cent, const float *ref, const int32_t *size, int C)
+{
+    double worst = 0.0;
+    for (int c = 0; c < C; ++c) {
+        if (size[c] <= 0)
+            continue;
+        double num = 0.0, den = 0.0;
+        for (int i = 0; i < d; ++i) {
+            double diff = (double)cent[(long)c * d + i] - (double)ref[(long)c * d + i];
+            num = num + diff * diff;
+            den = den + (double)ref[(long)c * d + i] * (double)ref[(long)c * d + i];
+        }
+        double r = den > 0.0 ? sqrt(num) / sqrt(den) : sqrt(num);
+        if (r > worst)
+            worst = r;
+    }
+    return worst;
+}

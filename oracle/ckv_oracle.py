@@ -70,6 +70,10 @@ def lib():
             L.ckvo_update.argtypes = [i32, P, i32, P, i32, P, P, P, P, P, i32,
                                       C.POINTER(C.c_long)]
             L.ckvo_update.restype = i32
+            L.ckvo_rebuild.argtypes = [i32, P, i32, P, P, P, i32, P]
+            L.ckvo_rebuild.restype = None
+            L.ckvo_drift.argtypes = [i32, P, P, P, i32]
+            L.ckvo_drift.restype = C.c_double
             _lib = L
     return _lib
 
@@ -159,6 +163,26 @@ def update(k_new: np.ndarray, cand: np.ndarray, cent: np.ndarray, size: np.ndarr
 # ---- a whole decode layer -----------------------------------------------------------
 
 ERR_CAPACITY = 1
+
+
+def rebuild(K: np.ndarray, members: np.ndarray, start: np.ndarray, size: np.ndarray):
+    """K [rows, d] (bf16 bits or fp32); CSR of C communities -> fp32 [C, d]."""
+    K = np.ascontiguousarray(K)
+    members = np.ascontiguousarray(members, np.int32)
+    start = np.ascontiguousarray(start, np.int32)
+    size = np.ascontiguousarray(size, np.int32)
+    C, d = size.shape[0], K.shape[1]
+    out = np.zeros((C, d), np.float32)
+    lib().ckvo_rebuild(d, _p(K), _dt(K), _p(members), _p(start), _p(size), C, _p(out))
+    return out
+
+
+def drift(cent: np.ndarray, ref: np.ndarray, size: np.ndarray) -> float:
+    """Largest relative L2 distance of cent from ref over non-empty communities."""
+    cent = np.ascontiguousarray(cent, np.float32)
+    ref = np.ascontiguousarray(ref, np.float32)
+    size = np.ascontiguousarray(size, np.int32)
+    return float(lib().ckvo_drift(cent.shape[1], _p(cent), _p(ref), _p(size), size.shape[0]))
 
 
 class OracleState:

@@ -51,6 +51,11 @@ MUTANTS = {
     "update-wrong-position": ("members[start[best] + size[best]] = n;",
                               "members[start[best] + size[best]] = n - 1;"),
     "update-no-square": ("dist = dist + diff * diff;", "dist = dist + diff;"),
+    "rebuild-skips-first-member": ("for (int m = 0; m < size[c]; ++m)\n                s = s + widen(K",
+                                   "for (int m = 1; m < size[c]; ++m)\n                s = s + widen(K"),
+    "rebuild-wrong-count": ("(float)(s / (double)size[c])", "(float)(s / (double)(size[c] + 1))"),
+    "drift-not-relative": ("double r = den > 0.0 ? sqrt(num) / sqrt(den) : sqrt(num);",
+                           "double r = sqrt(num);"),
 }
 
 

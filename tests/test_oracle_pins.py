@@ -378,3 +378,91 @@ def test_new_token_joins_its_generating_community_mostly():
         hit += int((res["assigned"] == L.step_labels[t].reshape(-1)).sum())
         tot += wl.NG
     assert hit / tot > 0.8
+
+
+# ------------------------------------------------- centroid rebuild and drift -------
+
+def _ulp_diff(a: np.ndarray, b: np.ndarray) -> int:
+    """Largest distance in fp32 units in the last place between two fp32 arrays."""
+    ia = a.astype(np.float32).view(np.int32).astype(np.int64)
+    ib = b.astype(np.float32).view(np.int32).astype(np.int64)
+    ia = np.where(ia < 0, -(ia & 0x7FFFFFFF), ia)
+    ib = np.where(ib < 0, -(ib & 0x7FFFFFFF), ib)
+    return int(np.abs(ia - ib).max()) if ia.size else 0
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_rebuild_is_member_mean(dt):
+    """Each rebuilt centroid is the longdouble mean of its member keys rounded to
+    fp32 (within one ulp: the fp64 sum rounds before the final rounding)."""
+    r = rng(31)
+    d, rows = 16, 300
+    K = r.standard_normal((rows, d)).astype(np.float32)
+    if dt == "bf16":
+        K = (K.view(np.uint32) >> 16).astype(np.uint16)
+    C = 12
+    size = r.integers(1, 40, size=C).astype(np.int32)
+    size[3] = 0
+    start = np.concatenate([[0], np.cumsum(size + 2)[:-1]]).astype(np.int32)
+    members = np.full(int((size + 2).sum()), -1, np.int32)
+    for c in range(C):
+        members[start[c]:start[c] + size[c]] = r.choice(rows, size[c], replace=False)
+    out = O.rebuild(K, members, start, size)
+    Kl = brute.bf16_bits_to_ld(K)
+    for c in range(C):
+        if size[c] == 0:
+            assert (out[c] == 0).all()
+            continue
+        ref = Kl[members[start[c]:start[c] + size[c]]].mean(0)
+        assert _ulp_diff(out[c], ref.astype(np.float32)) <= 1, c
+
+
+def test_rebuild_special_cases():
+    """A single member gives its key exactly; identical members give that key."""
+    K = np.array([[1.5, -2.25, 3.0], [7.0, 0.5, -1.0], [7.0, 0.5, -1.0], [7.0, 0.5, -1.0]],
+                 np.float32)
+    out = O.rebuild(K, np.array([0, 1, 2, 3], np.int32), np.array([0, 1], np.int32),
+                    np.array([1, 3], np.int32))
+    assert np.array_equal(out[0], K[0]) and np.array_equal(out[1], K[1])
+
+
+def test_rebuild_reproduces_generator_centroids():
+    """The generator's initial centroids (a torch fp64 mean, computed independently)
+    agree with the rebuild within one fp32 ulp."""
+    wl = I.make_workload(1, context=2048, steps=1)
+    st = H.oracle_state(wl)
+    L = wl.layers[0]
+    cent0 = L.centroids.cpu().numpy()
+    for g in range(wl.NG):
+        C = int(wl.layers[0].num_comms[g])
+        out = O.rebuild(st.K[0, g], st.members, st.start[g, :C], st.size[g, :C])
+        assert _ulp_diff(out, cent0[g, :C]) <= 1, g
+
+
+def test_drift_closed_forms():
+    ref = np.array([[3.0, 4.0], [1.0, 0.0], [0.0, 0.0]], np.float32)
+    size = np.array([1, 1, 0], np.int32)
+    assert O.drift(ref, ref, size) == 0.0
+    cent = ref.copy()
+    cent[0] = [3.3, 4.4]                         # 10% of |(3,4)| = 0.5 -> 0.1 relative
+    assert abs(O.drift(cent, ref, size) - 0.1) < 1e-6
+    cent[2] = [100.0, 100.0]                     # empty community: ignored
+    assert abs(O.drift(cent, ref, size) - 0.1) < 1e-6
+    cent[1] = [1.0, 0.5]                         # 0.5 relative beats 0.1
+    assert abs(O.drift(cent, ref, size) - 0.5) < 1e-6
+
+
+def test_running_centroids_drift_from_rebuild_within_rounding_bound():
+    """After local updates the running-mean centroids differ from a rebuild from the
+    member lists only by the per-update fp32 roundings."""
+    wl = I.make_workload(1, context=2048, steps=6)
+    st = H.oracle_state(wl)
+    init = st.size.copy()
+    for t in range(6):
+        q, kn, vn = H.step_inputs(wl, 0, t)
+        st.step(q, kn, vn, wl.budget, wl.scale, wl.M, H.max_index_len(wl))
+    for g in range(wl.NG):
+        C = int(st.num_comms[g])
+        reb = O.rebuild(st.K[0, g], st.members, st.start[g, :C], st.size[g, :C])
+        u = int((st.size[g, :C] - init[g, :C]).max())
+        assert O.drift(st.cent[g, :C], reb, st.size[g, :C]) <= (u + 2) * 2.0 ** -22
