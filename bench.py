@@ -145,6 +145,34 @@ def dense_baseline(layers, qkv, wl, scrub, args, elem):
                 steps=len(ms))
 
 
+def rebuild_timing(layers, scrub, args, elem):
+    """Maintenance path: centroids recomputed from the member lists (every member
+    key read once) and the drift of the running means from them, per layer, cold."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ms_r, ms_d, worst = [], [], 0.0
+    for t in range(4):
+        for lay in layers:
+            ref = torch.empty_like(lay.centroids)
+            if not args.warm:
+                scrub_sum = scrub.sum()
+            ev[0].record()
+            lay.rebuild(out=ref)
+            ev[1].record()
+            dr = lay.drift(ref)
+            ev[2].record()
+            torch.cuda.synchronize()
+            if t >= 1:
+                ms_r.append(ev[0].elapsed_time(ev[1]))
+                ms_d.append(ev[1].elapsed_time(ev[2]))
+                worst = max(worst, float(dr.max().item()))
+    lay = layers[0]
+    members = int(lay.comm_size.sum().item())
+    by = members * (lay.d * elem + 4 + 4) + lay.centroids.numel() * 4
+    mr = float(np.mean(ms_r))
+    return dict(ms_per_layer=mr, gbs=by / (mr / 1e3) / 1e9, bytes_per_layer=by,
+                drift_ms_per_layer=float(np.mean(ms_d)), max_drift=worst)
+
+
 def build_layers(wl, index_stride):
     layers = []
     for li in range(len(wl.layers)):
@@ -188,6 +216,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--scrub-mib", type=int, default=1024)
     ap.add_argument("--warm", action="store_true", help="no cache scrub between steps")
+    ap.add_argument("--no-rebuild", action="store_true",
+                    help="skip timing the centroid rebuild from the member lists")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-attention baseline (every cached token)")
     ap.add_argument("--seed", type=int, default=None)
@@ -265,6 +295,9 @@ def main():
         if t == 0 or (t + 1) % 10 == 0:
             log(f"[bench] step {t + 1}/{T}")
     wall = time.perf_counter() - wall0
+    rebuild = None
+    if not args.no_rebuild:
+        rebuild = rebuild_timing(layers, scrub, args, elem)
     dense = None
     if not args.no_dense:
         dense = dense_baseline(layers, qkv, wl, scrub, args, elem)
@@ -322,6 +355,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if rebuild is not None:
+        res["centroid_rebuild"] = rebuild
     if dense is not None:
         dense["sparse_speedup"] = dense["ms_per_step"] / (total_ms / K)
         res["dense_baseline"] = dense

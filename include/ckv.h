@@ -208,6 +208,33 @@ CKV_API ckv_status ckv_dense_decode_attn(const ckv_dims *dims, const void *q, co
                                          int32_t *err_flag, void *stream);
 
 /*
+ * Centroids recomputed from the member lists: for every community c < num_comms
+ * of every graph, mu_c = the mean of the keys of its members (stored member order,
+ * fp64 sums, one rounding to fp32; 0 for an empty community) -- the centre each
+ * community carries [RIT-graph], as a refresh when the running means of the local
+ * update have drifted over a long generation [RIT-plan: "Когда CommunityKV стоит
+ * включить в план инфраструктуры", drift of local assignments and periodic
+ * re-partitioning].  Keys are read through the page table of kv.
+ *   centroids_out : [NG][d/4][max_comms][4] fp32 (the layout of graphs->centroids);
+ *                   may be graphs->centroids itself (each output depends on keys only).
+ * err_flag: CKV_DEVERR_INDEX_RANGE when a member is outside [0, seq_len) or on an
+ * unmapped page (that member is left out of the sum, the count is not changed).
+ */
+CKV_API ckv_status ckv_rebuild_centroids(const ckv_dims *dims, const ckv_graphs *graphs,
+                                         const ckv_kv *kv, float *centroids_out,
+                                         int32_t *err_flag, void *stream);
+
+/*
+ * Drift of the running-mean centroids (graphs->centroids) from `reference` (same
+ * layout, e.g. the output of ckv_rebuild_centroids): drift[g] = the largest, over
+ * the non-empty communities of graph g, of ||mu_c - ref_c||_2 / ||ref_c||_2 (fp64,
+ * rounded to fp32; a zero reference row counts its absolute distance).
+ *   drift : [NG] fp32 (device)
+ */
+CKV_API ckv_status ckv_centroid_drift(const ckv_dims *dims, const ckv_graphs *graphs,
+                                      const float *reference, float *drift, void *stream);
+
+/*
  * One whole decode step, the four operations above in 4 kernel launches:
  * scoring; selection + compaction; sparse attention (split partials) with the
  * local update running in extra workgroups of the same launch (attention reads

@@ -71,6 +71,8 @@ def load(path: str = LIB_PATH):
                                   P, P, P, P, sz, P, P, P]),
         "ckv_dense_workspace_size": (sz, [pd, pk]),
         "ckv_dense_decode_attn": (i32, [pd, P, pk, C.c_float, P, P, sz, P, P]),
+        "ckv_rebuild_centroids": (i32, [pd, pg, pk, P, P, P]),
+        "ckv_centroid_drift": (i32, [pd, pg, P, P, P]),
         "ckv_status_string": (C.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -84,7 +86,7 @@ def load(path: str = LIB_PATH):
 EXPORTED = ("ckv_workspace_size", "ckv_centroids_from_rows", "ckv_centroids_to_rows",
             "ckv_score_centroids", "ckv_select", "ckv_sparse_decode_attn", "ckv_local_update",
             "ckv_decode_step", "ckv_dense_workspace_size", "ckv_dense_decode_attn",
-            "ckv_status_string")
+            "ckv_rebuild_centroids", "ckv_centroid_drift", "ckv_status_string")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -167,6 +169,17 @@ def ckv_dense_decode_attn(dims, q, kv, scale, out, ws, err_flag, stream=None):
     _check(load().ckv_dense_decode_attn(C.byref(dims), _ptr(q), C.byref(kv), scale, _ptr(out),
                                         _ptr(ws), ws.numel() * ws.element_size(), _ptr(err_flag),
                                         _stream(stream)), "ckv_dense_decode_attn")
+
+
+def ckv_rebuild_centroids(dims, graphs, kv, centroids_out, err_flag, stream=None):
+    _check(load().ckv_rebuild_centroids(C.byref(dims), C.byref(graphs), C.byref(kv),
+                                        _ptr(centroids_out), _ptr(err_flag), _stream(stream)),
+           "ckv_rebuild_centroids")
+
+
+def ckv_centroid_drift(dims, graphs, reference, drift, stream=None):
+    _check(load().ckv_centroid_drift(C.byref(dims), C.byref(graphs), _ptr(reference),
+                                     _ptr(drift), _stream(stream)), "ckv_centroid_drift")
 
 
 def ckv_local_update(dims, k_new, v_new, cand, n_cand, graphs, kv, assigned, err_flag,
@@ -274,6 +287,18 @@ class DecodeLayer:
             self.dense_ws = torch.empty(n, dtype=torch.uint8, device=self.out.device)
         out = self.out if out is None else out
         ckv_dense_decode_attn(self.dims, q, self.kv, scale, out, self.dense_ws, self.err)
+
+    def rebuild(self, out=None):
+        """Centroids recomputed from the member lists (interleaved layout)."""
+        out = torch.empty_like(self.centroids) if out is None else out
+        ckv_rebuild_centroids(self.dims, self.graphs, self.kv, out, self.err)
+        return out
+
+    def drift(self, reference):
+        """Per-graph largest relative distance of the running centroids from `reference`."""
+        d = torch.empty(self.NG, dtype=torch.float32, device=self.centroids.device)
+        ckv_centroid_drift(self.dims, self.graphs, reference, d)
+        return d
 
     def update(self, k_new, v_new):
         ckv_local_update(self.dims, k_new, v_new, self.cand, self.M, self.graphs, self.kv,

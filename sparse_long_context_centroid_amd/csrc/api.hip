@@ -161,6 +161,30 @@ ckv_status ckv_dense_decode_attn(const ckv_dims *dims, const void *q, const ckv_
     return hip_status(ckv::launch_dense_merge(p, *kv, out, static_cast<float *>(ws), st));
 }
 
+ckv_status ckv_rebuild_centroids(const ckv_dims *dims, const ckv_graphs *graphs,
+                                 const ckv_kv *kv, float *centroids_out, int32_t *err_flag,
+                                 void *stream) {
+    Problem p;
+    ckv_status s = make_problem(dims, p);
+    if (s != CKV_OK) return s;
+    if ((s = check_graphs(graphs)) != CKV_OK) return s;
+    if ((s = check_kv(kv, p)) != CKV_OK) return s;
+    if (!centroids_out) return CKV_ERR_INVALID_ARG;
+    return hip_status(ckv::launch_rebuild(p, *graphs, *kv, centroids_out, err_flag,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+ckv_status ckv_centroid_drift(const ckv_dims *dims, const ckv_graphs *graphs,
+                              const float *reference, float *drift, void *stream) {
+    Problem p;
+    ckv_status s = make_problem(dims, p);
+    if (s != CKV_OK) return s;
+    if ((s = check_graphs(graphs)) != CKV_OK) return s;
+    if (!reference || !drift) return CKV_ERR_INVALID_ARG;
+    return hip_status(
+        ckv::launch_drift(p, *graphs, reference, drift, static_cast<hipStream_t>(stream)));
+}
+
 ckv_status ckv_local_update(const ckv_dims *dims, const void *k_new, const void *v_new,
                             const int32_t *cand, int32_t n_cand, const ckv_graphs *graphs,
                             const ckv_kv *kv, int32_t *assigned, int32_t *err_flag,

@@ -99,6 +99,11 @@ hipError_t launch_dense_partials(const Problem &p, const void *q, const ckv_kv &
                                  float *partials, int32_t *err, hipStream_t st);
 hipError_t launch_dense_merge(const Problem &p, const ckv_kv &kv, float *out,
                               const float *partials, hipStream_t st);
+// Centroids recomputed from the member lists; drift of the running means.
+hipError_t launch_rebuild(const Problem &p, const ckv_graphs &gr, const ckv_kv &kv, float *out,
+                          int32_t *err, hipStream_t st);
+hipError_t launch_drift(const Problem &p, const ckv_graphs &gr, const float *ref, float *drift,
+                        hipStream_t st);
 hipError_t launch_update(const Problem &p, const void *k_new, const void *v_new,
                          const int32_t *cand, int n_cand, const ckv_graphs &gr, const ckv_kv &kv,
                          int32_t *assigned, int32_t *err, hipStream_t st);

@@ -100,10 +100,11 @@ def compare_state(layer: Bd.DecodeLayer, st, wl):
             _fail(f"graph {g}: centroids differ, max relative norm error {float((na / nb).max()):.3e}")
 
 
-def run_parity(wl, steps=None, li=0, index_stride=None, fused=False, log=print):
+def run_parity(wl, steps=None, li=0, index_stride=None, fused=False, log=print,
+               return_state=False):
     """Run `steps` decode steps of layer `li` on the GPU (the four C-ABI calls, or
     the fused ckv_decode_step) and in the oracle, and compare every step.
-    Returns a summary dict."""
+    Returns a summary dict (and the device layer and oracle state if asked)."""
     steps = wl.steps if steps is None else steps
     torch.cuda.synchronize()
     layer = Bd.decode_layer_from_workload(wl, li, index_stride=index_stride)
@@ -142,4 +143,6 @@ def run_parity(wl, steps=None, li=0, index_stride=None, fused=False, log=print):
                    mean_idx_len=float(layer.index_len.float().mean().item()))
     log(f"parity ok: {summary}")
     sys.stdout.flush()
+    if return_state:
+        return summary, layer, st
     return summary

@@ -193,3 +193,33 @@ def test_dense_baseline_matches_oracle(cfg, kw, sample):
         err = np.abs(out[b, h] - ref)
         rel = np.linalg.norm(out[b, h] - ref) / max(np.linalg.norm(ref), 1e-30)
         assert err.max() <= 2e-3 and rel <= 1e-3, (b, h, err.max(), rel)
+
+
+@pytest.mark.parametrize("cfg,kw", [
+    (1, dict(context=4096, steps=4)),
+    (4, dict(contexts=[5000, 2100, 8192, 777], steps=3, layers=1)),
+    (0, dict(steps=1)),
+])
+def test_rebuild_and_drift_match_oracle(cfg, kw):
+    """After some decode steps (members appended, centroids moved), the centroids
+    recomputed from the member lists are bit-exact with the oracle's, and the
+    per-graph drift of the running means agrees with the oracle's."""
+    import oracle.ckv_oracle as O
+    _case(f"rebuild cfg{cfg} {kw}")
+    wl = I.make_workload(cfg, device="cuda", **kw)
+    _, layer, st = run_parity(wl, fused=True, return_state=True)
+    reb = layer.rebuild()
+    drift = layer.drift(reb).cpu().numpy()
+    torch.cuda.synchronize()
+    assert int(layer.err.item()) == 0
+    rows = torch.empty((layer.NG, layer.Cmax, layer.d), dtype=torch.float32, device="cuda")
+    Bd.ckv_centroids_to_rows(layer.dims, reb, rows)
+    rows = rows.cpu().numpy()
+    for g in range(layer.NG):
+        b = g // (wl.Hkv * wl.gpk)
+        kvh = (g // wl.gpk) % wl.Hkv
+        C = int(st.num_comms[g])
+        ref = O.rebuild(st.K[b, kvh], st.members, st.start[g, :C], st.size[g, :C])
+        assert np.array_equal(rows[g, :C].view(np.uint32), ref.view(np.uint32)), g
+        dref = O.drift(st.cent[g, :C], ref, st.size[g, :C])
+        assert abs(float(drift[g]) - dref) <= 1e-5 * dref + 1e-12, (g, drift[g], dref)
