@@ -223,3 +223,58 @@ def test_rebuild_and_drift_match_oracle(cfg, kw):
         assert np.array_equal(rows[g, :C].view(np.uint32), ref.view(np.uint32)), g
         dref = O.drift(st.cent[g, :C], ref, st.size[g, :C])
         assert abs(float(drift[g]) - dref) <= 1e-5 * dref + 1e-12, (g, drift[g], dref)
+
+
+# Shapes beyond the five workloads: every (dtype, head_dim, heads-per-graph)
+# combination the library builds, in both graph modes.
+_SHAPES = [
+    I.ConfigSpec("bf16-d64-g8-group", 2, 16, 2, 64, 3000, False, 300, 3, I.DT_BF16),
+    I.ConfigSpec("bf16-d64-g8-perhead", 1, 16, 2, 64, 2000, True, 256, 2, I.DT_BF16),
+    I.ConfigSpec("fp32-d128-g2-perhead", 1, 4, 2, 128, 2500, True, 256, 3, I.DT_F32),
+    I.ConfigSpec("fp32-d128-g4-group", 2, 8, 2, 128, 2200, False, 200, 2, I.DT_F32),
+    I.ConfigSpec("bf16-d128-g1-mha", 2, 4, 4, 128, 2000, False, 200, 3, I.DT_BF16),
+    I.ConfigSpec("fp32-d64-g1-mha", 1, 2, 2, 64, 1500, False, 128, 2, I.DT_F32),
+    I.ConfigSpec("bf16-d128-g2-group", 3, 8, 4, 128, 1800, False, 160, 2, I.DT_BF16),
+    I.ConfigSpec("fp32-d64-g8-group", 1, 8, 1, 64, 2600, False, 256, 2, I.DT_F32),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["four-calls", "fused-step"])
+@pytest.mark.parametrize("spec", _SHAPES, ids=[s.name for s in _SHAPES])
+def test_parity_shapes(spec, fused):
+    _case(f"shape {spec.name} fused={fused}")
+    wl = I.make_workload(spec, device="cuda")
+    run_parity(wl, fused=fused)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["four-calls", "fused-step"])
+def test_parity_contexts_shorter_than_sinks(fused):
+    """Sequences of 3, 4 and 5 tokens (no communities, or only sinks) next to a
+    normal one: sinks only, no candidates, the token still appended."""
+    _case("short contexts")
+    wl = I.make_workload(1, device="cuda", contexts=[3, 4, 5, 700], steps=2)
+    run_parity(wl, fused=fused)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["four-calls", "fused-step"])
+def test_parity_empty_communities(fused):
+    """Communities of size 0 (members never listed) score -inf and are never kept
+    or candidates."""
+    _case("empty communities")
+    wl = I.make_workload(1, device="cuda", context=4096, steps=3)
+    L = wl.layers[0]
+    L.comm_size[:, 1:40:3] = 0
+    run_parity(wl, fused=fused)
+
+
+def test_parity_maximum_sizes():
+    """Near the largest community count (one 250K-token sequence: ~3900
+    communities, eight per select thread), the largest candidate count (16) and a
+    16K budget (86 attention splits per graph, past one merge load round)."""
+    _case("maximum sizes")
+    spec = I.ConfigSpec("max-sizes", 1, 4, 1, 128, 250000, False, 16384, 2, I.DT_BF16,
+                        n_cand=16)
+    wl = I.make_workload(spec, device="cuda")
+    assert wl.Cmax > 3584 and wl.Cmax <= 4096
+    run_parity(wl, fused=True)
+    run_parity(I.make_workload(spec, device="cuda"), fused=False)
