@@ -8,7 +8,7 @@
 //   cand   : the first n_cand communities of the same order (update candidates)
 //   list   : 0..min(S,n)-1, then members of kept communities in ascending id.
 //
-// One 512-thread workgroup per graph; thread t holds communities t*IPT ..
+// One 1024-thread workgroup per graph; thread t holds communities t*IPT ..
 // t*IPT+IPT-1 in registers, so every block scan runs in id order.
 //
 // The kept prefix is found without sorting.  Fast path: the scores are binned
@@ -31,7 +31,7 @@
 
 namespace ckv {
 
-constexpr int kSelThreads = 512;
+constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 
 template <int CTRL, int ROW_MASK = 0xF>
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
     // flat copy of the kept member lists: output slot p (0 <= p < total) belongs
     // to the compacted community e with list_off[e] <= p < list_off[e+1]
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 4;
     int top = 1;  // largest power of two <= ksel (ksel >= 1 whenever total > 0)
     while (top * 2 <= ksel) top *= 2;
     for (int p0 = 0; p0 < total; p0 += kBatch * kSelThreads) {
@@ -522,8 +522,7 @@ hipError_t launch_select(const Problem &p, const float *scores, const ckv_graphs
                            idx_len, num_sel, cand, selected, err);                              \
         return hipGetLastError();                                                               \
     }
-    CKV_SEL_CASE(1) CKV_SEL_CASE(2) CKV_SEL_CASE(3) CKV_SEL_CASE(4) CKV_SEL_CASE(6)
-    CKV_SEL_CASE(8)
+    CKV_SEL_CASE(1) CKV_SEL_CASE(2) CKV_SEL_CASE(3) CKV_SEL_CASE(4)
 #undef CKV_SEL_CASE
     return hipErrorInvalidValue;
 }
