@@ -33,6 +33,8 @@ namespace ckv {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
+// Longest kept-member list expanded into an LDS slot map (longer lists search).
+constexpr int kSelSrcMax = 8192;
 
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ int dpp_i(int x) {
@@ -204,6 +206,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __shared__ int scan_tmp[2 * kSelWaves];
     __shared__ int list_start[CKV_MAX_COMMS];
     __shared__ int list_off[CKV_MAX_COMMS + 1];
+    __shared__ int s_src[kSelSrcMax];
     __shared__ uint32_t cand_key[CKV_MAX_CAND];
     __shared__ int cand_id[CKV_MAX_CAND];
     __shared__ int cand_n;
@@ -458,33 +461,53 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         else overflow = true;
     }
     // flat copy of the kept member lists: output slot p (0 <= p < total) belongs
-    // to the compacted community e with list_off[e] <= p < list_off[e+1]
+    // to the compacted community e with list_off[e] <= p < list_off[e+1].  When the
+    // list fits s_src, each wave first expands its share of the communities into a
+    // slot -> pool-index map (LDS only); otherwise the slots find their community by
+    // lockstep binary searches.
     constexpr int kBatch = 4;
+    const bool mapped = total <= kSelSrcMax;
+    if (mapped) {
+        for (int e = w; e < ksel; e += kSelWaves) {
+            const int off = list_off[e], len = list_off[e + 1] - off, st0 = list_start[e];
+            for (int j = lane; j < len; j += kWave) s_src[off + j] = st0 + j;
+        }
+        __syncthreads();
+    }
     int top = 1;  // largest power of two <= ksel (ksel >= 1 whenever total > 0)
     while (top * 2 <= ksel) top *= 2;
     for (int p0 = 0; p0 < total; p0 += kBatch * kSelThreads) {
-        // last e with list_off[e] <= p, for the kBatch slots at once: the searches
-        // advance in lockstep, one LDS read per slot per halving step
-        int lo[kBatch];
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) lo[k] = 0;
-        for (int st = top; st > 0; st >>= 1) {
-            // branch-free: all kBatch LDS reads of a step are issued back to back
-            int v[kBatch];
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k) v[k] = list_off[min(lo[k] + st, ksel - 1)];
+        int src[kBatch];
+        if (mapped) {
 #pragma unroll
             for (int k = 0; k < kBatch; ++k) {
                 const int p = p0 + k * kSelThreads + tid;
-                lo[k] = (lo[k] + st < ksel && v[k] <= p) ? lo[k] + st : lo[k];
+                const int v = s_src[min(p, kSelSrcMax - 1)];  // read unconditionally
+                src[k] = p < total ? v : -1;
             }
-        }
-        int src[kBatch];
+        } else {
+            // last e with list_off[e] <= p, for the kBatch slots at once: the
+            // searches advance in lockstep, one LDS read per slot per halving step
+            int lo[kBatch];
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            const int p = p0 + k * kSelThreads + tid;
-            const int st0 = list_start[lo[k]], of0 = list_off[lo[k]];  // read unconditionally
-            src[k] = p < total ? st0 + (p - of0) : -1;
+            for (int k = 0; k < kBatch; ++k) lo[k] = 0;
+            for (int st = top; st > 0; st >>= 1) {
+                // branch-free: all kBatch LDS reads of a step are issued back to back
+                int v[kBatch];
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) v[k] = list_off[min(lo[k] + st, ksel - 1)];
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    const int p = p0 + k * kSelThreads + tid;
+                    lo[k] = (lo[k] + st < ksel && v[k] <= p) ? lo[k] + st : lo[k];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const int p = p0 + k * kSelThreads + tid;
+                const int st0 = list_start[lo[k]], of0 = list_off[lo[k]];  // unconditional
+                src[k] = p < total ? st0 + (p - of0) : -1;
+            }
         }
         // unconditional loads (slot 0 for idle lanes; total > 0 here, so the pool is
         // not empty): loads inside branches make the compiler wait for every
