@@ -296,3 +296,61 @@ double ckvo_drift(int d, const float *cent, const float *ref, const int32_t *siz
     }
     return worst;
 }
+
+/*
+ * Direct edges of the prefill token graph of one KV head [RIT-graph: the graph is
+ * built during the prefill pass from the QK^T scores the model computes anyway;
+ * a direct edge links a query to a key it attends strongly; the initial sink
+ * tokens are not graph nodes].  Readings: the strength of the link from query
+ * position i to key position j is the group score
+ *   z_ij = max over the KV head's G query heads of q_h[i] . k[j] * scale  (fp64),
+ * causal and without self-links (S <= j < i); the edges of query i are its
+ * `topk` strongest keys, in (z desc, j asc) order, fewer when i - S < topk.
+ *
+ *   Q     : query rows, head h of position i at Q + (i*G + h)*d    (dtype)
+ *   K     : key rows, position j at K + j*d                        (dtype)
+ *   rows  : the query positions to compute (nrows of them)
+ *   idx   : [nrows][topk] key positions, -1 padded;  score: [nrows][topk] fp32 z
+ */
+void ckvo_edges(int d, int G, const void *Q, const void *K, int dtype, int S, float scale,
+                int topk, const int32_t *rows, int nrows, int32_t *idx, float *score)
+{
+    for (int r = 0; r < nrows; ++r) {
+        int i = rows[r];
+        int32_t *oi = idx + (long)r * topk;
+        float *os = score + (long)r * topk;
+        for (int t = 0; t < topk; ++t) {
+            oi[t] = -1;
+            os[t] = -INFINITY;
+        }
+        int lo = S;
+        int cnt = i - lo > 0 ? i - lo : 0;
+        if (cnt == 0)
+            continue;
+        double *z = (double *)malloc(sizeof(double) * (size_t)cnt);
+        for (int j = lo; j < i; ++j) {
+            double best = -INFINITY;
+            for (int h = 0; h < G; ++h) {
+                double dot = 0.0;
+                for (int e = 0; e < d; ++e)
+                    dot = dot + widen(Q, ((long)i * G + h) * d + e, dtype) *
+                                widen(K, (long)j * d + e, dtype);
+                if (dot > best)
+                    best = dot;
+            }
+            z[j - lo] = best * (double)scale;
+        }
+        /* repeated extraction of the strongest remaining key (lowest j on ties) */
+        int k = topk < cnt ? topk : cnt;
+        for (int t = 0; t < k; ++t) {
+            int arg = -1;
+            for (int j = 0; j < cnt; ++j)
+                if (z[j] != -INFINITY && (arg < 0 || z[j] > z[arg]))
+                    arg = j;
+            oi[t] = lo + arg;
+            os[t] = (float)z[arg];
+            z[arg] = -INFINITY;
+        }
+        free(z);
+    }
+}

@@ -74,6 +74,8 @@ def lib():
             L.ckvo_rebuild.restype = None
             L.ckvo_drift.argtypes = [i32, P, P, P, i32]
             L.ckvo_drift.restype = C.c_double
+            L.ckvo_edges.argtypes = [i32, i32, P, P, i32, i32, C.c_float, i32, P, i32, P, P]
+            L.ckvo_edges.restype = None
             _lib = L
     return _lib
 
@@ -183,6 +185,20 @@ def drift(cent: np.ndarray, ref: np.ndarray, size: np.ndarray) -> float:
     ref = np.ascontiguousarray(ref, np.float32)
     size = np.ascontiguousarray(size, np.int32)
     return float(lib().ckvo_drift(cent.shape[1], _p(cent), _p(ref), _p(size), size.shape[0]))
+
+
+def edges(Q: np.ndarray, K: np.ndarray, S: int, scale: float, topk: int, rows=None):
+    """Q [n, G, d], K [n, d] (bf16 bits or fp32) of one KV head -> (idx, score)
+    [len(rows), topk]: each query position's strongest earlier non-sink keys."""
+    Q = np.ascontiguousarray(Q)
+    K = np.ascontiguousarray(K)
+    n, G, d = Q.shape
+    rows = np.arange(n, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
+    idx = np.empty((len(rows), topk), np.int32)
+    score = np.empty((len(rows), topk), np.float32)
+    lib().ckvo_edges(d, G, _p(Q), _p(K), _dt(K), int(S), scale, int(topk), _p(rows), len(rows),
+                     _p(idx), _p(score))
+    return idx, score
 
 
 class OracleState:

@@ -54,6 +54,16 @@ MUTANTS = {
     "rebuild-skips-first-member": ("for (int m = 0; m < size[c]; ++m)\n                s = s + widen(K",
                                    "for (int m = 1; m < size[c]; ++m)\n                s = s + widen(K"),
     "rebuild-wrong-count": ("(float)(s / (double)size[c])", "(float)(s / (double)(size[c] + 1))"),
+    "edges-self-link": ("int cnt = i - lo > 0 ? i - lo : 0;\n        if (cnt == 0)\n"
+                        "            continue;\n"
+                        "        double *z = (double *)malloc(sizeof(double) * (size_t)cnt);\n"
+                        "        for (int j = lo; j < i; ++j) {",
+                        "int cnt = i + 1 - lo > 0 ? i + 1 - lo : 0;\n        if (cnt == 0)\n"
+                        "            continue;\n"
+                        "        double *z = (double *)malloc(sizeof(double) * (size_t)cnt);\n"
+                        "        for (int j = lo; j <= i; ++j) {"),
+    "edges-include-sinks": ("int lo = S;\n        int cnt", "int lo = 0;\n        int cnt"),
+    "edges-tie-high-position": ("(arg < 0 || z[j] > z[arg])", "(arg < 0 || z[j] >= z[arg])"),
     "drift-not-relative": ("double r = den > 0.0 ? sqrt(num) / sqrt(den) : sqrt(num);",
                            "double r = sqrt(num);"),
 }

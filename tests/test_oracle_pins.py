@@ -466,3 +466,64 @@ def test_running_centroids_drift_from_rebuild_within_rounding_bound():
         reb = O.rebuild(st.K[0, g], st.members, st.start[g, :C], st.size[g, :C])
         u = int((st.size[g, :C] - init[g, :C]).max())
         assert O.drift(st.cent[g, :C], reb, st.size[g, :C]) <= (u + 2) * 2.0 ** -22
+
+
+# --------------------------------------------- prefill token-graph direct edges -----
+
+def _brute_edges(Q, K, S, scale, topk):
+    """Every causal non-sink score in longdouble, then a full sort."""
+    n, G, d = Q.shape
+    Ql, Kl = brute.bf16_bits_to_ld(Q), brute.bf16_bits_to_ld(K)
+    out = []
+    for i in range(n):
+        cand = []
+        for j in range(S, i):
+            z = max((Ql[i, h] * Kl[j]).sum() for h in range(G)) * brute.LD(np.float32(scale))
+            cand.append((-z, j))
+        cand.sort()
+        out.append([j for _, j in cand[:topk]])
+    return out
+
+
+@pytest.mark.parametrize("G,dt", [(1, "f32"), (4, "bf16"), (2, "f32")])
+def test_edges_brute_force(G, dt):
+    r = rng(60 + G)
+    n, d, S, topk = 40, 8, 4, 5
+    Q = r.standard_normal((n, G, d)).astype(np.float32)
+    K = r.standard_normal((n, d)).astype(np.float32)
+    if dt == "bf16":
+        Q = (Q.view(np.uint32) >> 16).astype(np.uint16)
+        K = (K.view(np.uint32) >> 16).astype(np.uint16)
+    idx, score = O.edges(Q, K, S, 0.3, topk)
+    want = _brute_edges(Q, K, S, 0.3, topk)
+    for i in range(n):
+        got = [int(j) for j in idx[i] if j >= 0]
+        assert got == want[i], (i, got, want[i])
+        assert all(S <= j < i for j in got)
+        assert (idx[i, len(got):] == -1).all()
+
+
+def test_edges_zero_query_takes_the_earliest_keys():
+    """All scores equal: the tie-break keeps the lowest positions past the sinks."""
+    n, d, S, topk = 30, 4, 4, 6
+    Q = np.zeros((n, 2, d), np.float32)
+    K = rng(3).standard_normal((n, d)).astype(np.float32)
+    idx, score = O.edges(Q, K, S, 0.5, topk)
+    for i in range(n):
+        k = min(topk, max(i - S, 0))
+        assert list(idx[i, :k]) == list(range(S, S + k))
+        assert (score[i, :k] == 0).all()
+
+
+def test_edges_group_is_max_of_heads():
+    """A key strongly linked to any head of the group is linked to the group."""
+    r = rng(9)
+    n, d, S = 24, 8, 2
+    Q = r.standard_normal((n, 3, d)).astype(np.float32)
+    K = r.standard_normal((n, d)).astype(np.float32)
+    _, sg = O.edges(Q, K, S, 1.0, 1)
+    best = np.full(n, -np.inf)
+    for h in range(3):
+        _, sh = O.edges(Q[:, h:h + 1].copy(), K, S, 1.0, 1)
+        best = np.maximum(best, sh[:, 0])
+    assert np.array_equal(sg[:, 0], best.astype(np.float32))
