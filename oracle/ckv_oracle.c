@@ -312,6 +312,27 @@ double ckvo_drift(int d, const float *cent, const float *ref, const int32_t *siz
  *   rows  : the query positions to compute (nrows of them)
  *   idx   : [nrows][topk] key positions, -1 padded;  score: [nrows][topk] fp32 z
  */
+/*
+ * The group score z_ij of the edges below for given pairs: query position rows[r],
+ * key position keys[r] (fp64, not rounded).
+ */
+void ckvo_edge_scores(int d, int G, const void *Q, const void *K, int dtype, float scale,
+                      const int32_t *rows, const int32_t *keys, int npairs, double *z)
+{
+    for (int r = 0; r < npairs; ++r) {
+        long i = rows[r], j = keys[r];
+        double best = -INFINITY;
+        for (int h = 0; h < G; ++h) {
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e)
+                dot = dot + widen(Q, (i * G + h) * d + e, dtype) * widen(K, j * d + e, dtype);
+            if (dot > best)
+                best = dot;
+        }
+        z[r] = best * (double)scale;
+    }
+}
+
 void ckvo_edges(int d, int G, const void *Q, const void *K, int dtype, int S, float scale,
                 int topk, const int32_t *rows, int nrows, int32_t *idx, float *score)
 {

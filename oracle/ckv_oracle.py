@@ -76,6 +76,8 @@ def lib():
             L.ckvo_drift.restype = C.c_double
             L.ckvo_edges.argtypes = [i32, i32, P, P, i32, i32, C.c_float, i32, P, i32, P, P]
             L.ckvo_edges.restype = None
+            L.ckvo_edge_scores.argtypes = [i32, i32, P, P, i32, C.c_float, P, P, i32, P]
+            L.ckvo_edge_scores.restype = None
             _lib = L
     return _lib
 
@@ -199,6 +201,21 @@ def edges(Q: np.ndarray, K: np.ndarray, S: int, scale: float, topk: int, rows=No
     lib().ckvo_edges(d, G, _p(Q), _p(K), _dt(K), int(S), scale, int(topk), _p(rows), len(rows),
                      _p(idx), _p(score))
     return idx, score
+
+
+def edge_scores(Q: np.ndarray, K: np.ndarray, scale: float, rows, keys) -> np.ndarray:
+    """fp64 group scores z of (query rows[r], key keys[r]) pairs, as in edges()."""
+    Q = np.ascontiguousarray(Q)
+    K = np.ascontiguousarray(K)
+    n, G, d = Q.shape
+    rows = np.ascontiguousarray(rows, np.int32)
+    keys = np.ascontiguousarray(keys, np.int32)
+    assert rows.shape == keys.shape and rows.ndim == 1
+    assert ((rows >= 0) & (rows < n) & (keys >= 0) & (keys < n)).all()
+    z = np.empty(len(rows), np.float64)
+    lib().ckvo_edge_scores(d, G, _p(Q), _p(K), _dt(K), scale, _p(rows), _p(keys), len(rows),
+                           _p(z))
+    return z
 
 
 class OracleState:

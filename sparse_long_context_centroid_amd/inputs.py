@@ -392,3 +392,48 @@ def _make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G, gpk, page_
                  q=torch.from_numpy(q).to(tdt).to(device),
                  k_new=torch.from_numpy(kn).to(tdt).to(device),
                  v_new=torch.from_numpy(vn).to(tdt).to(device), step_labels=zl)
+
+
+@dataclasses.dataclass
+class Prefill:
+    """Prefill queries and keys of one layer (bf16, contiguous)."""
+    q: torch.Tensor      # [B, n, Hq, d]
+    k: torch.Tensor      # [B, n, Hkv, d]
+    S: int
+    scale: float
+
+
+def make_prefill(seed: int, *, B: int, n: int, Hq: int, Hkv: int, d: int, S: int = 4,
+                 device: str = "cpu", mean_size: float = 64.0) -> Prefill:
+    """Seeded prefill Q/K with the community structure of the decode workloads.
+
+    Per (sequence, KV head): positions S.. carry Markov-scattered community labels
+    with geometric sizes (mean `mean_size`), each community a Gaussian centre;
+    a key is its community's centre + 0.3 noise (sinks: plain N(0, 1)).  The query
+    of head h at position i lies between the centre of its own position's
+    community and that of a uniformly drawn community, + 0.3 noise (a sink
+    position's own term is a random centre).  Bulk values are drawn with torch on
+    `device`."""
+    G = Hq // Hkv
+    q = torch.empty((B, n, Hq, d), dtype=torch.bfloat16, device=device)
+    k = torch.empty((B, n, Hkv, d), dtype=torch.bfloat16, device=device)
+    for b in range(B):
+        for kvh in range(Hkv):
+            rng = _ss(seed, 5, b, kvh)
+            N = max(n - S, 0)
+            lab, C = geometric_partition(rng, N, mean_size)
+            C = max(C, 1)
+            full = np.concatenate([rng.integers(0, C, size=min(S, n)), lab]).astype(np.int64)
+            other = rng.integers(0, C, size=(n, G)).astype(np.int64)
+            cen = torch.from_numpy(rng.standard_normal((C, d)).astype(np.float32)).to(device)
+            gk = _torch_gen(device, seed, 6, b, kvh)
+            lab_t = torch.from_numpy(full).to(device)
+            kn = torch.randn((n, d), generator=gk, device=device)
+            rows = cen[lab_t] + 0.3 * kn
+            rows[:min(S, n)] = kn[:min(S, n)]
+            k[b, :, kvh] = rows.to(torch.bfloat16)
+            oth = torch.from_numpy(other).to(device)
+            qn = torch.randn((n, G, d), generator=gk, device=device)
+            qq = 0.5 * (cen[lab_t][:, None, :] + cen[oth]) + 0.3 * qn
+            q[b, :, kvh * G:(kvh + 1) * G] = qq.to(torch.bfloat16)
+    return Prefill(q=q, k=k, S=S, scale=float(np.float32(1.0 / math.sqrt(d))))

@@ -62,6 +62,8 @@ MUTANTS = {
                         "            continue;\n"
                         "        double *z = (double *)malloc(sizeof(double) * (size_t)cnt);\n"
                         "        for (int j = lo; j <= i; ++j) {"),
+    "edge-scores-min-of-heads": ("            if (dot > best)\n                best = dot;\n        }\n        z[r]",
+                                 "            if (h == 0 || dot < best)\n                best = dot;\n        }\n        z[r]"),
     "edges-include-sinks": ("int lo = S;\n        int cnt", "int lo = 0;\n        int cnt"),
     "edges-tie-high-position": ("(arg < 0 || z[j] > z[arg])", "(arg < 0 || z[j] >= z[arg])"),
     "drift-not-relative": ("double r = den > 0.0 ? sqrt(num) / sqrt(den) : sqrt(num);",

@@ -527,3 +527,34 @@ def test_edges_group_is_max_of_heads():
         _, sh = O.edges(Q[:, h:h + 1].copy(), K, S, 1.0, 1)
         best = np.maximum(best, sh[:, 0])
     assert np.array_equal(sg[:, 0], best.astype(np.float32))
+
+
+def test_edge_scores_unit_queries_pick_key_entries():
+    """Head h of every query is c_h * e_{a_h}: its dot product with key j is
+    c_h * K[j][a_h] exactly, so the group score is scale * max_h c_h K[j][a_h]."""
+    r = rng(21)
+    n, d, G = 12, 8, 3
+    K = r.integers(-8, 9, size=(n, d)).astype(np.float32)
+    a = [1, 6, 3]
+    c = [1.0, -2.0, 0.5]
+    Q = np.zeros((n, G, d), np.float32)
+    for h in range(G):
+        Q[:, h, a[h]] = c[h]
+    rows = np.repeat(np.arange(n), n).astype(np.int32)
+    keys = np.tile(np.arange(n), n).astype(np.int32)
+    z = O.edge_scores(Q, K, 0.25, rows, keys)
+    for (i, j, zz) in zip(rows, keys, z):
+        want = 0.25 * max(c[h] * float(K[j, a[h]]) for h in range(G))
+        assert zz == want, (i, j, zz, want)
+
+
+def test_edge_scores_agree_with_the_edges_they_rank():
+    """The scores edges() reports for its chosen keys are these scores rounded."""
+    r = rng(22)
+    n, d, G, S, topk = 50, 16, 2, 3, 6
+    Q = r.standard_normal((n, G, d)).astype(np.float32)
+    K = r.standard_normal((n, d)).astype(np.float32)
+    idx, score = O.edges(Q, K, S, 0.7, topk)
+    rows, keys = np.nonzero(idx >= 0)
+    z = O.edge_scores(Q, K, 0.7, rows.astype(np.int32), idx[rows, keys])
+    assert np.array_equal(z.astype(np.float32), score[rows, keys])
