@@ -69,7 +69,7 @@ enum {
 };
 
 /* Largest supported values. */
-enum { CKV_MAX_COMMS = 4096, CKV_MAX_CAND = 16 };
+enum { CKV_MAX_COMMS = 4096, CKV_MAX_CAND = 16, CKV_MAX_EDGES = 8 };
 
 typedef struct ckv_dims {
     int32_t batch;         /* B sequences                                          */
@@ -233,6 +233,42 @@ CKV_API ckv_status ckv_rebuild_centroids(const ckv_dims *dims, const ckv_graphs 
  */
 CKV_API ckv_status ckv_centroid_drift(const ckv_dims *dims, const ckv_graphs *graphs,
                                       const float *reference, float *drift, void *stream);
+
+/*
+ * Direct edges of the prefill token graph, from the QK^T scores of the prefill
+ * [RIT-graph: the token graph is built during prefill from the QK^T the model
+ * computes anyway; one kind of edge links a query to a key it attends strongly,
+ * another links keys that are attended together; the initial sink tokens are
+ * not graph nodes].  Readings: graph g (the graphs of dims, graphs_per_kv) links
+ * query position i to key position j with strength
+ *   z_ij = max over the graph's query heads h of (q_h[i] . k[j]) * scale,
+ * causal and without self-links (num_sinks <= j < i); the direct edges of i are
+ * its `topk` strongest keys, in (z desc, j asc) order, fewer (padded with -1 and
+ * -inf) when i - num_sinks < topk; its co-attention pairs are all pairs of those
+ * keys, each as (lower position, higher position), listed in ascending order.
+ * Pairs are emitted per query, unaggregated: counting how often a pair recurs
+ * is left to the graph builder.  QK^T is computed on the matrix cores (bf16
+ * products, fp32 sums): keys whose z differ by less than the fp32 rounding of a
+ * d-term sum can swap places.
+ *   dims      : batch B (each of n positions), heads, head_dim, graphs_per_kv,
+ *               num_sinks; dtype must be CKV_DT_BF16 (else CKV_ERR_UNSUPPORTED);
+ *               max_comms is only validated
+ *   q         : [B][n][Hq][d] bf16 (prefill queries, contiguous)
+ *   k         : [B][n][Hkv][d] bf16 (prefill keys, contiguous)
+ *   topk      : 1 .. CKV_MAX_EDGES
+ *   edge_idx  : [NG][n][topk] int32 key positions (NG = B * Hkv * graphs_per_kv)
+ *   edge_score: [NG][n][topk] fp32 z
+ *   edge_pairs: NULL, or [NG][n][topk*(topk-1)/2][2] int32; a pair is (-1, -1)
+ *               when either key is missing
+ *   events    : NULL, or 2 hipEvent_t (as void*) with timing, bound to the
+ *               kernel's own start and end
+ * All buffers are the caller's device memory.  Returns CKV_ERR_INVALID_ARG for
+ * null buffers, n < 1, topk out of range or a non-finite scale.
+ */
+CKV_API ckv_status ckv_prefill_edges(const ckv_dims *dims, const void *q, const void *k,
+                                     int32_t n, int32_t topk, float scale, int32_t *edge_idx,
+                                     float *edge_score, int32_t *edge_pairs,
+                                     void *const *events, void *stream);
 
 /*
  * One whole decode step, the four operations above in 4 kernel launches:

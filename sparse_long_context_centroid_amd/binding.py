@@ -73,6 +73,7 @@ def load(path: str = LIB_PATH):
         "ckv_dense_decode_attn": (i32, [pd, P, pk, C.c_float, P, P, sz, P, P]),
         "ckv_rebuild_centroids": (i32, [pd, pg, pk, P, P, P]),
         "ckv_centroid_drift": (i32, [pd, pg, P, P, P]),
+        "ckv_prefill_edges": (i32, [pd, P, P, i32, i32, C.c_float, P, P, P, P, P]),
         "ckv_status_string": (C.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -86,7 +87,8 @@ def load(path: str = LIB_PATH):
 EXPORTED = ("ckv_workspace_size", "ckv_centroids_from_rows", "ckv_centroids_to_rows",
             "ckv_score_centroids", "ckv_select", "ckv_sparse_decode_attn", "ckv_local_update",
             "ckv_decode_step", "ckv_dense_workspace_size", "ckv_dense_decode_attn",
-            "ckv_rebuild_centroids", "ckv_centroid_drift", "ckv_status_string")
+            "ckv_rebuild_centroids", "ckv_centroid_drift", "ckv_prefill_edges",
+            "ckv_status_string")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -180,6 +182,22 @@ def ckv_rebuild_centroids(dims, graphs, kv, centroids_out, err_flag, stream=None
 def ckv_centroid_drift(dims, graphs, reference, drift, stream=None):
     _check(load().ckv_centroid_drift(C.byref(dims), C.byref(graphs), _ptr(reference),
                                      _ptr(drift), _stream(stream)), "ckv_centroid_drift")
+
+
+def ckv_prefill_edges(dims, q, k, n, topk, scale, edge_idx, edge_score, edge_pairs=None,
+                      events=None, stream=None):
+    """events: None or 2 torch.cuda.Event(enable_timing=True) bound to the kernel."""
+    ev = None
+    if events is not None:
+        if len(events) != 2:
+            raise CkvError("ckv_prefill_edges takes 2 events")
+        for e in events:
+            if e.cuda_event == 0:        # torch creates the HIP event at first record
+                e.record()
+        ev = (C.c_void_p * 2)(*[e.cuda_event for e in events])
+    _check(load().ckv_prefill_edges(C.byref(dims), _ptr(q), _ptr(k), n, topk, scale,
+                                    _ptr(edge_idx), _ptr(edge_score), _ptr(edge_pairs), ev,
+                                    _stream(stream)), "ckv_prefill_edges")
 
 
 def ckv_local_update(dims, k_new, v_new, cand, n_cand, graphs, kv, assigned, err_flag,

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libckv.so")
-SOURCES = ["api.hip", "score.hip", "select.hip", "attn.hip", "update.hip", "rebuild.hip"]
+SOURCES = ["api.hip", "score.hip", "select.hip", "attn.hip", "update.hip", "rebuild.hip", "edges.hip"]
 ARCH = os.environ.get("CKV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -2,6 +2,8 @@
 // launches on the caller's stream.  No allocation, no synchronisation, no state.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "ckv.h"
 #include "ckv_internal.h"
 
@@ -183,6 +185,25 @@ ckv_status ckv_centroid_drift(const ckv_dims *dims, const ckv_graphs *graphs,
     if (!reference || !drift) return CKV_ERR_INVALID_ARG;
     return hip_status(
         ckv::launch_drift(p, *graphs, reference, drift, static_cast<hipStream_t>(stream)));
+}
+
+ckv_status ckv_prefill_edges(const ckv_dims *dims, const void *q, const void *k, int32_t n,
+                             int32_t topk, float scale, int32_t *edge_idx, float *edge_score,
+                             int32_t *edge_pairs, void *const *events, void *stream) {
+    Problem p;
+    ckv_status s = make_problem(dims, p);
+    if (s != CKV_OK) return s;
+    if (p.dtype != CKV_DT_BF16) return CKV_ERR_UNSUPPORTED;
+    if (!q || !k || !edge_idx || !edge_score) return CKV_ERR_INVALID_ARG;
+    if (n < 1 || topk < 1 || topk > CKV_MAX_EDGES || !std::isfinite(scale))
+        return CKV_ERR_INVALID_ARG;
+    if ((long long)p.B * n * p.Hq * p.D >= (1LL << 40)) return CKV_ERR_INVALID_ARG;
+    if (events) {
+        p.ev_start = static_cast<hipEvent_t>(events[0]);
+        p.ev_stop = static_cast<hipEvent_t>(events[1]);
+    }
+    return hip_status(ckv::launch_edges(p, q, k, n, scale, topk, edge_idx, edge_score,
+                                        edge_pairs, static_cast<hipStream_t>(stream)));
 }
 
 ckv_status ckv_local_update(const ckv_dims *dims, const void *k_new, const void *v_new,

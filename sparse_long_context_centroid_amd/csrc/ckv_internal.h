@@ -104,6 +104,10 @@ hipError_t launch_rebuild(const Problem &p, const ckv_graphs &gr, const ckv_kv &
                           int32_t *err, hipStream_t st);
 hipError_t launch_drift(const Problem &p, const ckv_graphs &gr, const float *ref, float *drift,
                         hipStream_t st);
+// Prefill token graph: per-query top-k direct edges and their co-attention pairs.
+int edge_queries_per_block(const Problem &p);
+hipError_t launch_edges(const Problem &p, const void *q, const void *k, int n, float scale,
+                        int topk, int32_t *idx, float *score, int32_t *pairs, hipStream_t st);
 hipError_t launch_update(const Problem &p, const void *k_new, const void *v_new,
                          const int32_t *cand, int n_cand, const ckv_graphs &gr, const ckv_kv &kv,
                          int32_t *assigned, int32_t *err, hipStream_t st);

@@ -117,6 +117,28 @@ def test_dense_entry_points_validate(lib):
                                      1 << 30, fake, None) == -1
 
 
+def test_prefill_edges_validate(lib):
+    d = dims()
+    fake = C.c_void_p(0x1000)
+    nan = float("nan")
+    # null buffers, empty prefill, topk outside 1..8, non-finite scale
+    assert lib.ckv_prefill_edges(C.byref(d), None, fake, 64, 8, 0.1, fake, fake, None, None,
+                                 None) == -1
+    assert lib.ckv_prefill_edges(C.byref(d), fake, fake, 64, 8, 0.1, None, fake, None, None,
+                                 None) == -1
+    assert lib.ckv_prefill_edges(C.byref(d), fake, fake, 0, 8, 0.1, fake, fake, None, None,
+                                 None) == -1
+    for topk in (0, 9):
+        assert lib.ckv_prefill_edges(C.byref(d), fake, fake, 64, topk, 0.1, fake, fake, None,
+                                     None, None) == -1
+    assert lib.ckv_prefill_edges(C.byref(d), fake, fake, 64, 8, nan, fake, fake, None, None,
+                                 None) == -1
+    # fp32 operands are not built for the matrix-core kernel
+    f32 = dims(dtype=0)
+    assert lib.ckv_prefill_edges(C.byref(f32), fake, fake, 64, 8, 0.1, fake, fake, None, None,
+                                 None) == -2
+
+
 def test_status_strings(lib):
     for s, txt in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported configuration"),
                    (-3, "workspace missing or too small"), (-4, "HIP launch failed")]:
