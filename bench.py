@@ -173,6 +173,41 @@ def rebuild_timing(layers, scrub, args, elem):
                 drift_ms_per_layer=float(np.mean(ms_d)), max_drift=worst)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def edges_timing(wl, args):
+    """Prefill-side producer of the graph: per-query top-8 direct edges and their
+    co-attention pairs of one layer's prefill of one sequence at the workload's
+    longest context (ckv_prefill_edges), kernel-bound events, warm (the prefill's
+    Q and K outgrow the caches anyway).  Algorithmic work: q.k for every causal,
+    non-sink (query head, query, key) triple, 2 d flops each."""
+    n = int(wl.seq_len0.max())
+    pf = I.make_prefill(9000 + wl.seed, B=1, n=n, Hq=wl.Hq, Hkv=wl.Hkv, d=wl.d, S=wl.S,
+                        device="cuda")
+    topk = 8
+    NG = wl.Hkv * wl.gpk
+    dims = Bd.ckv_dims(1, wl.Hq, wl.Hkv, wl.d, wl.gpk, 64, wl.S, I.DT_BF16)
+    idx = torch.empty((NG, n, topk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((NG, n, topk), dtype=torch.float32, device="cuda")
+    pr = torch.empty((NG, n, topk * (topk - 1) // 2, 2), dtype=torch.int32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ms = []
+    for t in range(5):
+        Bd.ckv_prefill_edges(dims, pf.q, pf.k, n, topk, pf.scale, idx, sc, pr, events=ev)
+        torch.cuda.synchronize()
+        if t >= 2:
+            ms.append(ev[0].elapsed_time(ev[1]))
+    m = max(n - wl.S, 0)
+    flops = 2.0 * wl.d * wl.Hq * (m * (m - 1) / 2 + 0.0)
+    mean = float(np.mean(ms))
+    tf = flops / (mean / 1e3) / 1e12
+    return dict(kernel="edges_kernel", prefill_tokens=n, topk=topk, ms_per_layer=mean,
+                flops_per_layer=flops, tflops=tf, peak_tflops=MFMA_BF16_PEAK_TFLOPS,
+                frac_mfma_bf16=tf / MFMA_BF16_PEAK_TFLOPS,
+                prefill_tokens_per_s=n / (mean / 1e3))
+
+
 def build_layers(wl, index_stride):
     layers = []
     for li in range(len(wl.layers)):
@@ -220,6 +255,8 @@ def main():
                     help="skip timing the centroid rebuild from the member lists")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-attention baseline (every cached token)")
+    ap.add_argument("--no-edges", action="store_true",
+                    help="skip the prefill edge-extraction measurement")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before timing, run a plain device copy of this many MiB three times "
@@ -301,6 +338,9 @@ def main():
     dense = None
     if not args.no_dense:
         dense = dense_baseline(layers, qkv, wl, scrub, args, elem)
+    edges = None
+    if not args.no_edges:
+        edges = edges_timing(wl, args)
     err = max(int(l.err.item()) for l in layers)
     if err:
         raise SystemExit(f"device error flag {err} during the benchmark")
@@ -360,6 +400,8 @@ def main():
     if dense is not None:
         dense["sparse_speedup"] = dense["ms_per_step"] / (total_ms / K)
         res["dense_baseline"] = dense
+    if edges is not None:
+        res["prefill_edges"] = edges
     print(json.dumps(res), flush=True)
 
 

@@ -22,6 +22,13 @@ HIPCC_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
+# Per-file additions.  edges.hip: its scores are finite or -inf by construction,
+# so fmax needs no NaN quieting, and the MFMA accumulators stay in ordinary VGPRs
+# (no accumulator-register reads in the per-block filter); both measured faster.
+FILE_FLAGS = {
+    "edges.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
@@ -37,7 +44,8 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+               "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

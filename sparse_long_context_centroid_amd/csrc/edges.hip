@@ -25,14 +25,24 @@
 #include "ckv_device.h"
 #include "ckv_internal.h"
 
+#include <type_traits>
+
 namespace ckv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kEdgeWaves = 4;
-constexpr int kEdgeKT = 64;  // keys per LDS tile
+#ifndef CKV_EDGE_KT
+#define CKV_EDGE_KT 64
+#endif
+constexpr int kEdgeKT = CKV_EDGE_KT;  // keys per LDS tile
 constexpr int kEdgeList = 8; // list length kept per query (largest topk)
+#ifndef CKV_EDGE_REFRESH
+#define CKV_EDGE_REFRESH 4
+#endif
+constexpr int kEdgeRefresh = CKV_EDGE_REFRESH;  // tiles between row-bound refreshes
 constexpr int edge_queries_per_wave(int hpg) { return hpg <= 4 ? 16 : 8; }
 
 // (a, ia) before (b, ib) in the (score desc, position asc) order.
@@ -62,6 +72,21 @@ __device__ __forceinline__ void edge_insert(float (&ts)[kEdgeList], int (&ti)[kE
     }
 }
 
+// The 8th largest of the values held by the 16 lanes of a row, in every lane of
+// the row (a bitonic sort across the row, descending by lane, then a broadcast).
+__device__ __forceinline__ float row16_eighth_largest(float v, int r16) {
+#pragma unroll
+    for (int k = 2; k <= 16; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const float o = __shfl_xor(v, j, 16);
+            const bool keep_max = ((r16 & j) == 0) == ((r16 & k) == 0);
+            v = keep_max ? fmaxf(v, o) : fminf(v, o);
+        }
+    }
+    return __shfl(v, 7, 16);
+}
+
 template <int D, int HPG>
 __global__ __launch_bounds__(kEdgeWaves * kWave) void edges_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, int n, int Hq, int Hkv, int gpk,
@@ -76,9 +101,12 @@ __global__ __launch_bounds__(kEdgeWaves * kWave) void edges_kernel(
     constexpr int QPL = 4 / HL;                        // queries per lane per M-block
     constexpr int NQ = MB * QPL;                       // query slots per lane (= 4)
     constexpr int LDSR = D + 8;                        // LDS row stride in bf16
+    constexpr int KT = kEdgeKT;
+    constexpr int kPieces = KT * D / 8 / (kEdgeWaves * kWave);  // 16-byte loads per thread
     static_assert(HPG == 1 || HPG == 2 || HPG == 4 || HPG == 8, "heads per graph");
     static_assert(NQ == 4, "query slots");
-    __shared__ __align__(16) bf16_t s_k[kEdgeKT * LDSR];
+    static_assert(kPieces * kEdgeWaves * kWave * 8 == KT * D, "tile split");
+    __shared__ __align__(16) bf16_t s_k[2][KT * LDSR];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -100,15 +128,13 @@ __global__ __launch_bounds__(kEdgeWaves * kWave) void edges_kernel(
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
         const int R = m * 16 + r16;
-        const int qi = qw + R / HPG, h = R % HPG;
+        // queries past n read row n-1 (their results are not written)
+        const int qi = min(qw + R / HPG, n - 1), h = R % HPG;
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (qi < n)
-                u = *reinterpret_cast<const uint4 *>(qb + ((size_t)qi * Hq + h0 + h) * D +
-                                                     32 * t + 8 * g4);
-            a[m][t] = __builtin_bit_cast(bf16x8_t, u);
-        }
+        for (int t = 0; t < T; ++t)
+            a[m][t] = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const uint4 *>(qb + ((size_t)qi * Hq + h0 + h) * D +
+                                                           32 * t + 8 * g4));
     }
     // query of slot s = m*QPL + jq: accumulator rows 4g4 + jq*HL .. +HL of block m
     int qpos[NQ];
@@ -126,62 +152,147 @@ __global__ __launch_bounds__(kEdgeWaves * kWave) void edges_kernel(
             ts[s][p] = -__builtin_inff();
             ti[s][p] = -1;
         }
+    // thr[s]: a key of slot s can only matter if its score is above thr[s] = the
+    // larger of this lane's 8th entry and a lower bound of the row's 8th best
+    // (keys arrive in ascending position, so an equal score loses the tie)
+    float thr[NQ];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) thr[s] = -__builtin_inff();
 
     const int qlast = min(q0 + QPB, n) - 1;  // largest query of the workgroup
     const int wlast = min(qw + QPW, n) - 1;  // ... of this wave
-    for (int kt = S; kt < qlast; kt += kEdgeKT) {
-        // stage keys kt .. kt+63 (zeros past n)
-        __syncthreads();
-        constexpr int kChunks = kEdgeKT * D / 8;  // 16-byte pieces of a tile
+    // key tiles S, S+KT, ... below qlast; tile it+1 is fetched into registers
+    // while tile it is computed, then stored into the other LDS buffer.  Rows
+    // past n are clamped to row n-1: such keys are only ever compared for
+    // queries past n, whose results are not written.
+    u32x4_t pre[kPieces];
+    // one 16-key block on the matrix cores: T MFMAs per M-block
+    auto mma = [&](const bf16_t *sk, f32x4_t (&acc)[MB]) __attribute__((always_inline)) {
+        // B operand: lane (r16, g4) holds elements 32t + 8g4 .. +8 of key k16 + r16
+        bf16x8_t bb[T];
 #pragma unroll
-        for (int c = tid; c < kChunks; c += kEdgeWaves * kWave) {
-            const int row = c / (D / 8), col = c % (D / 8);
-            const int j = kt + row;
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (j < n)
-                u = *reinterpret_cast<const uint4 *>(kb_ + ((size_t)j * Hkv + kvh) * D + 8 * col);
-            *reinterpret_cast<uint4 *>(s_k + row * LDSR + 8 * col) = u;
-        }
-        __syncthreads();
-        for (int sb = 0; sb < kEdgeKT; sb += 16) {
-            const int k16 = kt + sb;
-            if (k16 >= wlast) break;  // every key from here on is at or past the wave's queries
-            // B operand: lane (r16, g4) holds elements 32t + 8g4 .. +8 of key k16 + r16
-            bf16x8_t bb[T];
+        for (int t = 0; t < T; ++t)
+            bb[t] = *reinterpret_cast<const bf16x8_t *>(sk + r16 * LDSR + 32 * t + 8 * g4);
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < T; ++t)
-                bb[t] = *reinterpret_cast<const bf16x8_t *>(s_k + (sb + r16) * LDSR + 32 * t +
-                                                            8 * g4);
-            const int j = k16 + r16;  // this lane's accumulator column
-            f32x4_t acc[MB];
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][t], bb[t], acc[m], 0, 0, 0);
+        }
+    };
+    // the block's group max, scale and list filter (MASKED applies j < i: only
+    // tiles that reach the wave's queries); one wave-wide branch per block
+    auto filter = [&](const f32x4_t (&acc)[MB], int k16, auto masked_c)
+                      __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_c)::value;
+        const int j = k16 + r16;  // this lane's accumulator column
+        float zs[NQ];
+        bool ins[NQ];
+        bool any = false;
 #pragma unroll
-            for (int m = 0; m < MB; ++m) {
-                acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < MB; ++m) {
 #pragma unroll
-                for (int t = 0; t < T; ++t)
-                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][t], bb[t], acc[m], 0, 0, 0);
+            for (int jq = 0; jq < QPL; ++jq) {
+                float z = acc[m][jq * HL];
+#pragma unroll
+                for (int h = 1; h < HL; ++h) z = fmaxf(z, acc[m][jq * HL + h]);
+                if constexpr (HPG == 8) {
+                    // the other four heads sit in the lane 16 apart
+                    const uint32_t u = __float_as_uint(z);
+                    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+                    z = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+                }
+                const int s = m * QPL + jq;
+                z *= scale;
+                if constexpr (MASKED) z = j < qpos[s] ? z : -__builtin_inff();
+                zs[s] = z;
+                ins[s] = z > thr[s];
+                any |= ins[s];
             }
+        }
+        if (__ballot(any)) {
 #pragma unroll
-            for (int m = 0; m < MB; ++m) {
-#pragma unroll
-                for (int jq = 0; jq < QPL; ++jq) {
-                    float z = acc[m][jq * HL];
-#pragma unroll
-                    for (int h = 1; h < HL; ++h) z = fmaxf(z, acc[m][jq * HL + h]);
-                    if constexpr (HPG == 8) {
-                        // the other four heads sit in the lane 16 apart
-                        const uint32_t u = __float_as_uint(z);
-                        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-                        z = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-                    }
-                    const int s = m * QPL + jq;
-                    z = j < qpos[s] ? z * scale : -__builtin_inff();
-                    const bool ins = z > ts[s][EK - 1];
-                    if (__ballot(ins)) {
-                        if (ins) edge_insert<true>(ts[s], ti[s], z, j);
-                    }
+            for (int s = 0; s < NQ; ++s) {
+                if (ins[s]) {
+                    edge_insert<true>(ts[s], ti[s], zs[s], j);
+                    thr[s] = fmaxf(thr[s], ts[s][EK - 1]);
                 }
             }
+        }
+    };
+    // the blocks of a tile, software-pipelined: block b+1's MFMAs are issued
+    // before block b is filtered, so the matrix cores run under the filter
+    auto tile = [&](const bf16_t *sk, int kt, int nb, auto masked_c) __attribute__((always_inline)) {
+        static_assert(KT == 64, "four blocks per tile");
+        f32x4_t x0[MB], x1[MB];
+        mma(sk, x0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nb > 1) mma(sk + 16 * LDSR, x1);
+        filter(x0, kt, masked_c);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nb > 2) mma(sk + 32 * LDSR, x0);
+        if (nb > 1) filter(x1, kt + 16, masked_c);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nb > 3) mma(sk + 48 * LDSR, x1);
+        if (nb > 2) filter(x0, kt + 32, masked_c);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nb > 3) filter(x1, kt + 48, masked_c);
+    };
+    const int ntiles = qlast > S ? (qlast - S + KT - 1) / KT : 0;
+    // Tile it is stored into LDS buffer it & 1 at the top of iteration it, from
+    // registers loaded during iteration it-1's compute (a loop-carried prefetch,
+    // which the compiler cannot sink next to the store).  One barrier per tile:
+    // the buffer written at the top of iteration it was last read in iteration
+    // it-2, which every wave finished before the barrier of iteration it-1.
+    // Piece p of a tile: row (tid + 256p) / (D/8), 16-byte column (tid + 256p) % (D/8);
+    // rows are clamped to n-1 (the last prefetch re-reads valid rows).
+#pragma unroll
+    for (int p = 0; p < kPieces; ++p) {
+        const int c = tid + p * kEdgeWaves * kWave;
+        const int j = min(S + c / (D / 8), n - 1);
+        pre[p] = *reinterpret_cast<const u32x4_t *>(kb_ + ((size_t)j * Hkv + kvh) * D +
+                                                  8 * (c % (D / 8)));
+    }
+    // the A operands are complete before the loop (an empty use of each): left in
+    // flight, they make the compiler wait for every outstanding load -- the next
+    // tile's included -- at the first MFMA of every tile
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int t = 0; t < T; ++t) asm volatile("" ::"v"(a[m][t]));
+#pragma unroll 1
+    for (int it = 0; it < ntiles; ++it) {
+        const int kt = S + it * KT;
+        bf16_t *sk = s_k[it & 1];
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p) {
+            const int c = tid + p * kEdgeWaves * kWave;
+            *reinterpret_cast<u32x4_t *>(sk + (c / (D / 8)) * LDSR + 8 * (c % (D / 8))) = pre[p];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p) {
+            const int c = tid + p * kEdgeWaves * kWave;
+            const int j = min(kt + KT + c / (D / 8), n - 1);
+            pre[p] = *reinterpret_cast<const u32x4_t *>(kb_ + ((size_t)j * Hkv + kvh) * D +
+                                                      8 * (c % (D / 8)));
+        }
+        // blocks of this tile below the wave's last query (wave-uniform)
+        const int nb = min(max((wlast - kt + 15) / 16, 0), KT / 16);
+        if (nb > 0) {
+            if (kt + KT <= qw)
+                tile(sk, kt, nb, std::integral_constant<bool, false>{});
+            else
+                tile(sk, kt, nb, std::integral_constant<bool, true>{});
+        }
+        // row bound: the 8 largest lane maxima are 8 distinct keys, so the row's
+        // 8th best is at least the 8th largest of the 16 maxima (refreshed every
+        // kEdgeRefresh tiles: it tightens slowly once the lists have filled)
+        if (it % kEdgeRefresh == kEdgeRefresh - 1) {
+#pragma unroll
+            for (int s = 0; s < NQ; ++s)
+                thr[s] = fmaxf(thr[s], row16_eighth_largest(ts[s][0], r16));
         }
     }
 
