@@ -12,9 +12,18 @@ a thread pool (ctypes releases the GIL during each C call).
 
 Graph numbering follows the GQA layout: graph g = (b*Hkv + kvh)*gpk + j, where
 gpk = 1 (one graph per query group: heads kvh*G .. kvh*G+G-1 share it) or
-gpk = G (one graph per query head, j = head index inside the group)
-(rit.work post "CommunityKV long-context decoding", section on how many graphs a
-model keeps).
+gpk = G (one graph per query head, j = head index inside the group), or gpk = 0:
+one graph per layer (graph g = sequence b), shared by every head of the layer
+(rit.work post "CommunityKV long-context decoding", sections on how many graphs a
+model keeps and where to start: the group graph, the per-head graph, and the
+whole layer in one graph, which the post reports as the least accurate).
+
+Readings for the layer graph: a community holds one centroid per KV head (the
+mean of its members' keys in that head), stored as one row of Hkv*d values,
+KV head after KV head; its score is the max over all query heads of
+q_h . mu_{c, kv head of h} * scale (the group reading, over the whole layer);
+one index list serves every KV head; the new token joins the nearest candidate
+in squared L2 over the whole row (all KV heads' keys, in that order).
 """
 from __future__ import annotations
 
@@ -221,7 +230,7 @@ def edge_scores(Q: np.ndarray, K: np.ndarray, scale: float, rows, keys) -> np.nd
 class OracleState:
     """Host state of one decode layer, advanced one step at a time.
 
-    centroids [NG, Cmax, d] fp32; num_comms [NG]; comm_start/size/cap [NG, Cmax];
+    centroids [NG, Cmax, d] fp32 ([B, Cmax, Hkv*d] for the layer graph); num_comms [NG]; comm_start/size/cap [NG, Cmax];
     members [pool]; K, V [B, Hkv, n_alloc, d] raw (uint16 bf16 bits or float32),
     logical token order; seq_len [B].
     """
@@ -230,7 +239,8 @@ class OracleState:
                  comm_size, comm_cap, members, K, V, seq_len, threads=None):
         self.B, self.Hq, self.Hkv, self.d, self.gpk, self.S = B, Hq, Hkv, d, gpk, S
         self.G = Hq // Hkv
-        self.NG = B * Hkv * gpk
+        self.layer = gpk == 0
+        self.NG = B if self.layer else B * Hkv * gpk
         self.cent = np.array(centroids, np.float32, copy=True, order="C")
         self.num_comms = np.array(num_comms, np.int32, copy=True)
         self.start = np.array(comm_start, np.int32, copy=True, order="C")
@@ -243,13 +253,41 @@ class OracleState:
         self.threads = threads or len(os.sched_getaffinity(0))
 
     def heads_of(self, g: int):
+        if self.layer:
+            return list(range(self.Hq))
         j = g % self.gpk
         kvh = (g // self.gpk) % self.Hkv
         if self.gpk == 1:
             return list(range(kvh * self.G, (kvh + 1) * self.G))
         return [kvh * self.G + j]
 
+    def _layer_step(self, g, q, k_new, budget, scale, M, max_len, res):
+        """One whole-layer graph (g = sequence b)."""
+        b, d, G = g, self.d, self.G
+        n = int(self.seq_len[b])
+        Cn = int(self.num_comms[g])
+        size = self.size[g, :Cn].copy()
+        # per KV head: its G heads against its slice of the centroid rows; the max
+        # of the fp32-rounded scores equals the rounding of the max (rounding is
+        # monotone)
+        s = np.full(Cn, -np.inf, np.float32)
+        for kvh in range(self.Hkv):
+            part = np.ascontiguousarray(self.cent[g, :Cn, kvh * d:(kvh + 1) * d])
+            s = np.maximum(s, score(q[b, kvh * G:(kvh + 1) * G], part, size, scale))
+        sel, k, cand = select(s, size, int(budget[b]), M)
+        idx = index_list(n, self.S, sel, self.start[g, :Cn], size, self.members, max_len)
+        outs = {}
+        for kvh in range(self.Hkv):
+            for h in range(kvh * G, (kvh + 1) * G):
+                outs[h] = attend(q[b, h], self.K[b, kvh], self.V[b, kvh], idx, scale)
+        r, _ = update(np.ascontiguousarray(k_new[b]).reshape(-1), cand, self.cent[g, :Cn],
+                      self.size[g, :Cn], self.cap[g, :Cn], self.start[g, :Cn], self.members,
+                      n) if Cn else (-2, 0)
+        res[g] = (s, sel, k, cand, idx, outs, r)
+
     def _graph_step(self, g, q, k_new, budget, scale, M, max_len, res):
+        if self.layer:
+            return self._layer_step(g, q, k_new, budget, scale, M, max_len, res)
         b = g // (self.Hkv * self.gpk)
         kvh = (g // self.gpk) % self.Hkv
         n = int(self.seq_len[b])
@@ -290,7 +328,7 @@ class OracleState:
             "err": np.zeros(self.NG, np.int32),
         }
         for g, (s, sel, k, cand, idx, outs, r) in enumerate(res):
-            b = g // (self.Hkv * self.gpk)
+            b = g if self.layer else g // (self.Hkv * self.gpk)
             Cn = len(s)
             out["scores"][g, :Cn] = s
             out["selected"][g, :Cn] = sel

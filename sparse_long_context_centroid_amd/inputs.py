@@ -55,6 +55,18 @@ class ConfigSpec:
     ctx_hi: int = 0
     layers: int = 1
     shuffled_pages: bool = False
+    layer_graph: bool = False     # one graph per layer, shared by all heads
+
+
+def granularity_spec(base: ConfigSpec, mode: str) -> ConfigSpec:
+    """The same workload with another graph granularity: "group" (one graph per KV
+    head), "head" (one per query head) or "layer" (one per layer)."""
+    if mode not in ("group", "head", "layer"):
+        raise ValueError(mode)
+    stem = base.name.rsplit("-", 1)[0] if base.name.endswith(("-group", "-perhead")) else base.name
+    tag = {"group": "group", "head": "perhead", "layer": "layergraph"}[mode]
+    return dataclasses.replace(base, name=f"{stem}-{tag}", per_head_graphs=mode == "head",
+                               layer_graph=mode == "layer")
 
 
 CONFIGS: List[ConfigSpec] = [
@@ -75,7 +87,8 @@ def torch_dtype(dt: int):
 @dataclasses.dataclass
 class Layer:
     """One layer's graph state and KV pool."""
-    centroids: torch.Tensor       # [NG, Cmax, d] fp32, natural row layout
+    centroids: torch.Tensor       # [NG, Cmax, d] fp32, natural row layout ([B, Cmax, Hkv*d]
+                                  # for the layer graph: one centroid per KV head, in order)
     num_comms: np.ndarray         # [NG] int32
     comm_start: np.ndarray        # [NG, Cmax] int32, offset into `members`
     comm_size: np.ndarray         # [NG, Cmax] int32
@@ -100,7 +113,7 @@ class Workload:
     Hq: int
     Hkv: int
     d: int
-    gpk: int                      # graphs per KV head (1 or Hq/Hkv)
+    gpk: int                      # graphs per KV head (1 or Hq/Hkv; 0: one per layer)
     S: int
     M: int
     dtype: int
@@ -118,7 +131,7 @@ class Workload:
 
     @property
     def NG(self) -> int:
-        return self.B * self.Hkv * self.gpk
+        return self.B if self.gpk == 0 else self.B * self.Hkv * self.gpk
 
 
 def _ss(seed: int, *key: int) -> np.random.Generator:
@@ -199,7 +212,7 @@ def make_workload(cfg: int | ConfigSpec, seed: Optional[int] = None, *, device: 
     d = spec.head_dim
     Hq, Hkv = spec.num_q_heads, spec.num_kv_heads
     G = Hq // Hkv
-    gpk = G if spec.per_head_graphs else 1
+    gpk = G if spec.per_head_graphs else (0 if spec.layer_graph else 1)
     slack = T if slack is None else slack
     rng0 = _ss(seed, 0)
     if contexts is not None:
@@ -267,12 +280,33 @@ def _pad_communities(layer: Layer, Cmax: int) -> None:
 
 def _make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G, gpk, page_table,
                 num_pages, tdt, device) -> Layer:
-    NG = B * Hkv * gpk
+    layer = gpk == 0
+    NG = B if layer else B * Hkv * gpk
+    gps = 1 if layer else Hkv * gpk           # graphs per sequence
+    cd = Hkv * d if layer else d              # centroid row length
     # --- structure: per (b, kvh) base labels, per graph member lists -------------
     base_labels, centres, graph_labels = [], [], []
     Cs = []
     for b in range(B):
         n = int(ns[b])
+        if layer:
+            # one partition of the sequence, one centre per community and KV head
+            rng = _ss(seed, 1, li, b, 0)
+            N = max(n - S, 0)
+            if spec.markov_labels:
+                C = spec.markov_labels
+                lab = markov_labels(rng, N, C)
+            else:
+                lab, C = geometric_partition(rng, N)
+            full = np.full(n, -1, np.int32)
+            full[min(S, n):] = lab
+            for kvh in range(Hkv):
+                base_labels.append(full)
+                centres.append(_ss(seed, 8, li, b, kvh).standard_normal((max(C, 1), d))
+                               .astype(np.float32))
+            graph_labels.append(lab)
+            Cs.append(C)
+            continue
         for kvh in range(Hkv):
             rng = _ss(seed, 1, li, b, kvh)
             N = max(n - S, 0)
@@ -303,7 +337,7 @@ def _make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G, gpk, page_
     pools = []
     off = 0
     for g in range(NG):
-        b = g // (Hkv * gpk)
+        b = g // gps
         lj = graph_labels[g]
         C = Cs[g]
         size = np.bincount(lj, minlength=C).astype(np.int32) if C else np.zeros(0, np.int32)
@@ -326,7 +360,7 @@ def _make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G, gpk, page_
     # --- bulk keys / values on the device, written into the paged pool ----------
     k_pages = torch.zeros((num_pages, Hkv, PAGE_SIZE, d), dtype=tdt, device=device)
     v_pages = torch.zeros_like(k_pages)
-    centroids = torch.zeros((NG, Cmax, d), dtype=torch.float32, device=device)
+    centroids = torch.zeros((NG, Cmax, cd), dtype=torch.float32, device=device)
     for b in range(B):
         n = int(ns[b])
         npg = (n + PAGE_SIZE - 1) // PAGE_SIZE
@@ -351,6 +385,17 @@ def _make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G, gpk, page_
         # initial centroids: fp64 mean of the stored member keys, rounded to fp32
         for kvh in range(Hkv):
             k64 = kb[kvh, :n].to(torch.float64)
+            if layer:
+                C = Cs[b]
+                if C == 0:
+                    continue
+                lab = torch.from_numpy(graph_labels[b].astype(np.int64)).to(device)
+                ssum = torch.zeros((C, d), dtype=torch.float64, device=device)
+                ssum.index_add_(0, lab, k64[min(S, n):])
+                cnt = torch.from_numpy(comm_size[b, :C].astype(np.float64)).to(device)
+                centroids[b, :C, kvh * d:(kvh + 1) * d] = \
+                    (ssum / cnt.clamp(min=1)[:, None]).to(torch.float32)
+                continue
             for j in range(gpk):
                 g = (b * Hkv + kvh) * gpk + j
                 C = Cs[g]
@@ -369,6 +414,29 @@ def _make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G, gpk, page_
     vn = np.zeros((T, B, Hkv, d), np.float32)
     zl = np.zeros((T, B, Hkv), np.int32)
     for b in range(B):
+        if layer:
+            # one label sequence per sequence, shared by its KV heads
+            rz = _ss(seed, 9, li, b)
+            lab = base_labels[b * Hkv]
+            C = centres[b * Hkv].shape[0]
+            z = int(lab[-1]) if len(lab) and lab[-1] >= 0 else int(rz.integers(C))
+            for t in range(T):
+                if rz.random() >= 0.7:
+                    z = int(rz.integers(C))
+                zl[t, b, :] = z
+            for kvh in range(Hkv):
+                rng = _ss(seed, 4, li, b, kvh)
+                cen = centres[b * Hkv + kvh]
+                for t in range(T):
+                    z = int(zl[t, b, kvh])
+                    kn[t, b, kvh] = cen[z] + 0.3 * rng.standard_normal(d)
+                    vn[t, b, kvh] = rng.standard_normal(d)
+                    for j in range(G):
+                        other = int(rng.integers(C - 1)) if C > 1 else 0
+                        if C > 1 and other >= z:
+                            other += 1
+                        q[t, b, kvh * G + j] = cen[z] + cen[other] + 0.3 * rng.standard_normal(d)
+            continue
         for kvh in range(Hkv):
             rng = _ss(seed, 4, li, b, kvh)
             lab = base_labels[b * Hkv + kvh]

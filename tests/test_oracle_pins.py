@@ -558,3 +558,122 @@ def test_edge_scores_agree_with_the_edges_they_rank():
     rows, keys = np.nonzero(idx >= 0)
     z = O.edge_scores(Q, K, 0.7, rows.astype(np.int32), idx[rows, keys])
     assert np.array_equal(z.astype(np.float32), score[rows, keys])
+
+
+# ------------------------------------------------- whole-layer graph (gpk = 0) ------
+
+def _layer_state_from(st_group, wl):
+    """The same arrays read as one graph per layer (valid when Hkv = 1)."""
+    return O.OracleState(B=wl.B, Hq=wl.Hq, Hkv=wl.Hkv, d=wl.d, gpk=0, S=wl.S,
+                         centroids=st_group.cent, num_comms=st_group.num_comms,
+                         comm_start=st_group.start, comm_size=st_group.size,
+                         comm_cap=st_group.cap, members=st_group.members, K=st_group.K,
+                         V=st_group.V, seq_len=st_group.seq_len)
+
+
+def test_layer_graph_with_one_kv_head_is_the_group_graph():
+    """With a single KV head the layer graph and the group graph are the same graph:
+    every result of several steps must agree exactly."""
+    wl = I.make_workload(0, steps=3)              # 4 query heads, 1 KV head
+    assert wl.Hkv == 1 and wl.gpk == 1
+    grp = H.oracle_state(wl)
+    lay = _layer_state_from(grp, wl)
+    for t in range(3):
+        q, kn, vn = H.step_inputs(wl, 0, t)
+        a = grp.step(q, kn, vn, wl.budget, wl.scale, wl.M, H.max_index_len(wl))
+        b = lay.step(q, kn, vn, wl.budget, wl.scale, wl.M, H.max_index_len(wl))
+        for key in ("scores", "selected", "kstar", "cand", "idx_len", "assigned", "err"):
+            assert np.array_equal(a[key], b[key]), (t, key)
+        assert all(np.array_equal(x, y) for x, y in zip(a["idx"], b["idx"]))
+        assert np.array_equal(a["out"], b["out"])
+    assert np.array_equal(grp.cent, lay.cent) and np.array_equal(grp.size, lay.size)
+
+
+def test_layer_graph_of_replicated_kv_heads_matches_one_head():
+    """Two KV heads holding identical keys, values, queries and centroid halves: the
+    layer graph must score, select, attend and assign exactly as the group graph of
+    one of them, and move both centroid halves as that graph moves its centroid."""
+    wl = I.make_workload(1, context=1024, steps=3)
+    L = wl.layers[0]
+    one = H.oracle_state(wl)
+    # graph 0 of the group workload = KV head 0 (heads 0..3); keep only that head
+    G, d = wl.Hq // wl.Hkv, wl.d
+    Cn = int(one.num_comms[0])
+    mk = lambda Hkv, cent, K, V: O.OracleState(
+        B=1, Hq=G * Hkv, Hkv=Hkv, d=d, gpk=1 if Hkv == 1 else 0, S=wl.S, centroids=cent,
+        num_comms=one.num_comms[:1], comm_start=one.start[:1], comm_size=one.size[:1],
+        comm_cap=one.cap[:1], members=one.members, K=K, V=V, seq_len=one.seq_len)
+    single = mk(1, one.cent[:1], one.K[:, :1], one.V[:, :1])
+    double = mk(2, np.concatenate([one.cent[:1], one.cent[:1]], axis=2),
+                np.concatenate([one.K[:, :1]] * 2, axis=1), np.concatenate([one.V[:, :1]] * 2, axis=1))
+    for t in range(3):
+        q, kn, vn = H.step_inputs(wl, 0, t)
+        q1, kn1, vn1 = q[:, :G], kn[:, :1], vn[:, :1]
+        q2 = np.concatenate([q1, q1], axis=1)
+        kn2, vn2 = np.concatenate([kn1, kn1], axis=1), np.concatenate([vn1, vn1], axis=1)
+        a = single.step(q1, kn1, vn1, wl.budget, wl.scale, wl.M, H.max_index_len(wl))
+        b = double.step(q2, kn2, vn2, wl.budget, wl.scale, wl.M, H.max_index_len(wl))
+        for key in ("scores", "selected", "kstar", "cand", "idx_len", "assigned"):
+            assert np.array_equal(a[key], b[key]), (t, key)
+        assert np.array_equal(a["idx"][0], b["idx"][0])
+        assert np.array_equal(b["out"][0, :G], a["out"][0]) and np.array_equal(b["out"][0, G:], a["out"][0])
+    assert np.array_equal(double.cent[0, :Cn, :d], single.cent[0, :Cn])
+    assert np.array_equal(double.cent[0, :Cn, d:], single.cent[0, :Cn])
+    assert np.array_equal(double.K[0, 1], single.K[0, 0])
+
+
+def test_layer_graph_centroids_stay_member_means():
+    """Layer graph over 8 distinct KV heads: after local updates every KV head's
+    slice of every centroid is the mean of the members' keys in that head (so the
+    new token's key lands in every head and in the right slice)."""
+    spec = I.granularity_spec(I.CONFIGS[1], "layer")
+    steps = 12
+    wl = I.make_workload(spec, context=1024, steps=steps)
+    assert wl.gpk == 0 and wl.NG == 1
+    st = H.oracle_state(wl)
+    init = st.size.copy()
+    for t in range(steps):
+        q, kn, vn = H.step_inputs(wl, 0, t)
+        res = st.step(q, kn, vn, wl.budget, wl.scale, wl.M, H.max_index_len(wl))
+        assert res["assigned"][0] >= 0
+    d = wl.d
+    moved = 0
+    for c in range(int(st.num_comms[0])):
+        sz = int(st.size[0, c])
+        if sz == 0:
+            continue
+        mem = st.members[st.start[0, c]:st.start[0, c] + sz]
+        u = sz - int(init[0, c])
+        moved += u
+        for kvh in range(wl.Hkv):
+            mean = brute.bf16_bits_to_ld(st.K[0, kvh])[mem].mean(0)
+            got = st.cent[0, c, kvh * d:(kvh + 1) * d].astype(brute.LD)
+            err = np.linalg.norm((got - mean).astype(np.float64))
+            tol = (u + 1) * 2.0 ** -22 * float(np.linalg.norm(mean.astype(np.float64))) + 1e-30
+            assert err <= tol, (c, kvh, u, err, tol)
+    assert moved == steps
+
+
+def test_layer_graph_score_is_max_over_all_heads_of_their_own_head_slice():
+    """Brute force (longdouble): each query head is scored against the centroid
+    slice of its own KV head, and the layer score is the max over all heads."""
+    spec = I.granularity_spec(I.CONFIGS[1], "layer")
+    wl = I.make_workload(spec, context=1024, steps=1)
+    st = H.oracle_state(wl)
+    q, kn, vn = H.step_inputs(wl, 0, 0)
+    C = int(st.num_comms[0])
+    cent = st.cent[0, :C].copy()
+    res = st.step(q, kn, vn, wl.budget, wl.scale, wl.M, H.max_index_len(wl))
+    d, G = wl.d, wl.Hq // wl.Hkv
+    ql = brute.bf16_bits_to_ld(q[0])
+    cl = cent.astype(brute.LD)
+    want = np.full(C, -np.inf)
+    for h in range(wl.Hq):
+        kvh = h // G
+        dots = (cl[:, kvh * d:(kvh + 1) * d] * ql[h]).sum(1) * brute.LD(wl.scale)
+        want = np.maximum(want, dots.astype(np.float64))
+    want[st.size[0, :C] == 0] = -np.inf
+    got = res["scores"][0, :C].astype(np.float64)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin)
+    assert np.allclose(got[fin], want[fin], rtol=2e-7, atol=1e-6)
