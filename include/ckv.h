@@ -12,6 +12,10 @@
  *   [RIT-granul] same post, section "Ускорение зависит от того, сколько графов
  *                хранит модель": one graph per group of heads sharing K/V, or one
  *                per query head; a small active token budget.
+ *   [RIT-plan]   same post, section "Когда CommunityKV стоит включить в план
+ *                инфраструктуры": drift of local assignments, periodic
+ *                re-partitioning, the group graph as the starting point and the
+ *                whole-layer graph as the less accurate variant.
  *   [ABSTRACT]   "CommunityKV: Efficient Long-Context Decoding via Graph
  *                Partitioning" (McKenna et al., 2026), abstract: constant-time
  *                local update rule, per-head and query-group graphs.
@@ -76,19 +80,42 @@ typedef struct ckv_dims {
     int32_t num_q_heads;   /* Hq                                                   */
     int32_t num_kv_heads;  /* Hkv; Hq % Hkv == 0, G = Hq/Hkv in {1,2,4,8}           */
     int32_t head_dim;      /* d in {64, 128}                                       */
-    int32_t graphs_per_kv; /* 1 (query-group graph) or G (one graph per query head) */
+    int32_t graphs_per_kv; /* 1 (query-group graph), G (one graph per query head),  */
+                           /* or 0 (one graph per layer, shared by all heads; see   */
+                           /* "Graph granularity" below)                            */
     int32_t max_comms;     /* Cmax: stride of per-community arrays; multiple of 64, */
                            /* <= CKV_MAX_COMMS                                      */
     int32_t num_sinks;     /* S >= 0: positions 0..S-1 are attention sinks          */
     int32_t dtype;         /* CKV_DT_BF16 or CKV_DT_F32: q, K, V, k_new, v_new      */
 } ckv_dims;
 
+/*
+ * Graph granularity [RIT-granul: one graph per group of heads that share keys and
+ * values is the fast default; one graph per query head is slower and needs more
+ * memory.  RIT-plan: putting a whole layer into one graph was clearly less
+ * accurate].
+ * graph g of a batch, NG graphs:
+ *   graphs_per_kv = 1: g = b*Hkv + kvh, heads kvh*G .. kvh*G+G-1, NG = B*Hkv
+ *   graphs_per_kv = G: g = (b*Hkv + kvh)*G + j, head kvh*G + j,    NG = B*Hq
+ *   graphs_per_kv = 0: g = b, every head of the layer,              NG = B
+ * Readings for the layer graph: a community carries one centroid per KV head (a
+ * centroid row of Hkv*d values, KV head after KV head, the centroid of KV head kvh
+ * at elements kvh*d .. kvh*d+d-1); its score is the max over all query heads of
+ * q_h . (head kvh(h)'s centroid) * scale; one index list serves every KV head;
+ * the new token's key row (its Hkv keys, in order) joins the nearest candidate in
+ * squared L2 over the whole row, and every KV head's K/V row n is written.  The
+ * layer graph's update stages M centroid rows in LDS: M*(Hkv*d+4)*4 + Hkv*d*8
+ * bytes must fit in 64 KiB, else CKV_ERR_UNSUPPORTED.  ckv_prefill_edges does not
+ * take the layer graph.
+ */
+
 /* Community state of NG graphs.  Community c of graph g owns member slots
  * members[comm_start[g*Cmax+c] .. + comm_cap[g*Cmax+c]); the first
  * comm_size[g*Cmax+c] hold token positions in ascending order of insertion. */
 typedef struct ckv_graphs {
     float *centroids;    /* fp32, "community-interleaved": element i of centroid c of
-                            graph g at centroids[((g*(d/4) + i/4)*Cmax + c)*4 + i%4] */
+                            graph g at centroids[((g*(R/4) + i/4)*Cmax + c)*4 + i%4],
+                            R = d (R = Hkv*d for the layer graph)              */
     int32_t *num_comms;  /* [NG] communities in use, C_g <= Cmax                     */
     int32_t *comm_start; /* [NG*Cmax]                                                 */
     int32_t *comm_size;  /* [NG*Cmax]                                                 */

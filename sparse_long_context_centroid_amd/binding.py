@@ -249,7 +249,10 @@ class DecodeLayer:
         self.dims = make_dims(B, Hq, Hkv, d, gpk, Cmax, S, dtype)
         self.B, self.Hq, self.Hkv, self.d, self.gpk, self.S, self.M = B, Hq, Hkv, d, gpk, S, M
         self.Cmax = Cmax
-        self.NG = B * Hkv * gpk
+        # gpk = 0: one graph per layer (per sequence) whose centroid rows hold one
+        # d-slice per KV head
+        self.NG = B if gpk == 0 else B * Hkv * gpk
+        self.cdim = Hkv * d if gpk == 0 else d
         self.page_size = page_size
         t = lambda a: torch.as_tensor(a).to(**i32).contiguous()
         self.num_comms = t(num_comms)
@@ -257,7 +260,8 @@ class DecodeLayer:
         self.comm_size = t(comm_size)
         self.comm_cap = t(comm_cap)
         self.members = t(members)
-        self.centroids = torch.empty(self.NG * Cmax * d, dtype=torch.float32, device=dev)
+        self.centroids = torch.empty(self.NG * Cmax * self.cdim, dtype=torch.float32,
+                                     device=dev)
         rows = centroid_rows.to(dev, torch.float32).contiguous()
         ckv_centroids_from_rows(self.dims, rows, self.centroids)
         self.k = k_pages.to(dev).contiguous()
@@ -330,14 +334,14 @@ class DecodeLayer:
         self.update(k_new, v_new)
 
     def step_fused(self, q, k_new, v_new, scale, events=None):
-        """The same step through ckv_decode_step (4 launches)."""
+        """The same step through ckv_decode_step (4 launches; 5 for the layer graph)."""
         ckv_decode_step(self.dims, q, k_new, v_new, self.graphs, self.kv, self.budget, self.M,
                         scale, self.scores, self.index_list, self.index_len, self.num_selected,
                         self.cand, self.selected, self.assigned, self.out, self.ws, self.err,
                         events=events)
 
     def centroid_rows(self) -> torch.Tensor:
-        rows = torch.empty((self.NG, self.Cmax, self.d), dtype=torch.float32,
+        rows = torch.empty((self.NG, self.Cmax, self.cdim), dtype=torch.float32,
                            device=self.centroids.device)
         ckv_centroids_to_rows(self.dims, self.centroids, rows)
         return rows

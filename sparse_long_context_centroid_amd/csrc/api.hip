@@ -20,7 +20,8 @@ ckv_status make_problem(const ckv_dims *d, Problem &p) {
         return CKV_ERR_INVALID_ARG;
     if (d->num_q_heads % d->num_kv_heads != 0) return CKV_ERR_INVALID_ARG;
     const int G = d->num_q_heads / d->num_kv_heads;
-    if (d->graphs_per_kv != 1 && d->graphs_per_kv != G) return CKV_ERR_INVALID_ARG;
+    if (d->graphs_per_kv != 0 && d->graphs_per_kv != 1 && d->graphs_per_kv != G)
+        return CKV_ERR_INVALID_ARG;
     if (G != 1 && G != 2 && G != 4 && G != 8) return CKV_ERR_UNSUPPORTED;
     if (d->head_dim != 64 && d->head_dim != 128) return CKV_ERR_UNSUPPORTED;
     if (d->dtype != CKV_DT_BF16 && d->dtype != CKV_DT_F32) return CKV_ERR_UNSUPPORTED;
@@ -33,7 +34,7 @@ ckv_status make_problem(const ckv_dims *d, Problem &p) {
     p.Cmax = d->max_comms;
     p.S = d->num_sinks;
     p.dtype = d->dtype;
-    if ((long long)p.NG() * p.Cmax * p.D > (1LL << 40)) return CKV_ERR_INVALID_ARG;
+    if ((long long)p.NG() * p.Cmax * p.cdim() > (1LL << 40)) return CKV_ERR_INVALID_ARG;
     return CKV_OK;
 }
 
@@ -59,7 +60,8 @@ ckv_status hip_status(hipError_t e) { return e == hipSuccess ? CKV_OK : CKV_ERR_
 
 // The split merge keeps one weight per (head, split) in LDS.
 ckv_status check_splits(const Problem &p, int index_stride) {
-    const size_t lds = (size_t)p.heads_per_graph() * ckv::attn_max_splits(p, index_stride) * 4;
+    const Problem a = ckv::attn_problem(p);
+    const size_t lds = (size_t)a.heads_per_graph() * ckv::attn_max_splits(a, index_stride) * 4;
     return lds <= 65536 ? CKV_OK : CKV_ERR_UNSUPPORTED;
 }
 
@@ -193,7 +195,7 @@ ckv_status ckv_prefill_edges(const ckv_dims *dims, const void *q, const void *k,
     Problem p;
     ckv_status s = make_problem(dims, p);
     if (s != CKV_OK) return s;
-    if (p.dtype != CKV_DT_BF16) return CKV_ERR_UNSUPPORTED;
+    if (p.dtype != CKV_DT_BF16 || p.layer()) return CKV_ERR_UNSUPPORTED;
     if (!q || !k || !edge_idx || !edge_score) return CKV_ERR_INVALID_ARG;
     if (n < 1 || topk < 1 || topk > CKV_MAX_EDGES || !std::isfinite(scale))
         return CKV_ERR_INVALID_ARG;
@@ -217,6 +219,7 @@ ckv_status ckv_local_update(const ckv_dims *dims, const void *k_new, const void 
     if ((s = check_kv(kv, p)) != CKV_OK) return s;
     if (!k_new || !v_new || !cand || !assigned) return CKV_ERR_INVALID_ARG;
     if (n_cand < 1 || n_cand > CKV_MAX_CAND) return CKV_ERR_INVALID_ARG;
+    if (p.layer() && !ckv::layer_update_fits(p, n_cand)) return CKV_ERR_UNSUPPORTED;
     return hip_status(ckv::launch_update(p, k_new, v_new, cand, n_cand, *graphs, *kv, assigned,
                                          err_flag, static_cast<hipStream_t>(stream)));
 }
@@ -238,6 +241,7 @@ ckv_status ckv_decode_step(const ckv_dims *dims, const void *q, const void *k_ne
         return CKV_ERR_INVALID_ARG;
     if (n_cand < 1 || n_cand > CKV_MAX_CAND || index_stride < 1) return CKV_ERR_INVALID_ARG;
     if ((s = check_splits(p, index_stride)) != CKV_OK) return s;
+    if (p.layer() && !ckv::layer_update_fits(p, n_cand)) return CKV_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < ckv_workspace_size(dims, index_stride)) return CKV_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     // launch k's timing events, bound to the kernel's own start and end
@@ -256,6 +260,21 @@ ckv_status ckv_decode_step(const ckv_dims *dims, const void *q, const void *k_ne
                                            index_list, index_stride, index_len, num_selected,
                                            cand, selected, err_flag, st))) != CKV_OK)
         return s;
+    if (p.layer()) {
+        // the layer graph: attention, then its own update launch (no bump), then the
+        // merge with the seq_len advance
+        if ((s = hip_status(ckv::launch_attn_partials(timed(2), q, *kv, index_list,
+                                                      index_stride, index_len, scale,
+                                                      static_cast<float *>(ws), err_flag,
+                                                      nullptr, st))) != CKV_OK)
+            return s;
+        if ((s = hip_status(ckv::launch_layer_update(p, k_new, v_new, cand, n_cand, *graphs,
+                                                     *kv, assigned, err_flag, false, st))) !=
+            CKV_OK)
+            return s;
+        return hip_status(ckv::launch_attn_merge(timed(3), index_stride, out,
+                                                 static_cast<float *>(ws), kv->seq_len, st));
+    }
     const ckv::UpdateSpec upd{k_new, v_new, cand, n_cand, graphs, assigned};
     if ((s = hip_status(ckv::launch_attn_partials(timed(2), q, *kv, index_list, index_stride,
                                                   index_len, scale, static_cast<float *>(ws),

@@ -152,7 +152,8 @@ __global__ __launch_bounds__(256) void attn_kernel(
     const T *__restrict__ q, T *__restrict__ kc, T *__restrict__ vc,
     const int32_t *__restrict__ page_table, int log2ps, int max_pages, int num_pages,
     int32_t *__restrict__ seq_len, const int32_t *__restrict__ idx, int idx_stride,
-    const int32_t *__restrict__ idx_len, int Hq, int Hkv, int gpk, float scale_log2,
+    int list_div, const int32_t *__restrict__ idx_len, int Hq, int Hkv, int gpk,
+    float scale_log2,
     float *__restrict__ part, int max_splits, int chunks_per_wg, int32_t *__restrict__ err,
     UpdateArgs u) {
     constexpr int EPL = 16 / sizeof(T);     // row elements per lane
@@ -201,7 +202,9 @@ __global__ __launch_bounds__(256) void attn_kernel(
     const int kvh = (g / gpk) % Hkv;
     const int h0 = kvh * G + (gpk == 1 ? 0 : g % gpk);
     const int n = seq_len[b];
-    const int len = MODE == kAttnDense ? n : min(idx_len[g], idx_stride);
+    // index list of this graph (one list serves list_div consecutive graphs)
+    const int gl = g / list_div;
+    const int len = MODE == kAttnDense ? n : min(idx_len[gl], idx_stride);
     const int span = CH * chunks_per_wg;  // tokens one workgroup may cover
     const int nsplit = (len + span - 1) / span;
     if (split >= nsplit) {
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
         const int te = c0 + t;
         int row = -1;
         if (te < c_end) {
-            const int pos = MODE == kAttnDense ? te : idx[(size_t)g * idx_stride + te];
+            const int pos = MODE == kAttnDense ? te : idx[(size_t)gl * idx_stride + te];
             if (pos >= 0 && pos < n) {
                 const int lp = pos >> log2ps;
                 const int pg = lp < max_pages ? page_table[(size_t)b * max_pages + lp] : -1;
@@ -503,7 +506,7 @@ static void launch_partials_t(const Problem &p, const void *q, const ckv_kv &kv,
                           st, p.ev_start, p.ev_stop, 0, static_cast<const T *>(q),
                           static_cast<T *>(kv.k), static_cast<T *>(kv.v), kv.page_table,
                           log2_pow2(kv.page_size), kv.max_pages_per_seq, kv.num_pages,
-                          kv.seq_len, idx, idx_stride, idx_len, p.Hq, p.Hkv, p.gpk,
+                          kv.seq_len, idx, idx_stride, p.list_div, idx_len, p.Hq, p.Hkv, p.gpk,
                           scale * kLog2e, partials, ms, cpw, err, u);
 }
 
@@ -539,10 +542,12 @@ static hipError_t launch_mode(const Problem &p, int mode, const void *q, const c
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_partials(const Problem &p, const void *q, const ckv_kv &kv,
+hipError_t launch_attn_partials(const Problem &pg, const void *q, const ckv_kv &kv,
                                 const int32_t *idx, int idx_stride, const int32_t *idx_len,
                                 float scale, float *partials, int32_t *err, const UpdateSpec *upd,
                                 hipStream_t st) {
+    if (upd && pg.layer()) return hipErrorInvalidValue;  // the layer graph updates apart
+    const Problem p = attn_problem(pg);
     UpdateArgs u{};
     if (upd) {
         u = UpdateArgs{upd->k_new, upd->v_new, upd->cand, upd->n_cand, upd->graphs->centroids,
@@ -579,8 +584,9 @@ static hipError_t launch_merge(const Problem &p, int ms, float *out, const float
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_merge(const Problem &p, int idx_stride, float *out, const float *partials,
+hipError_t launch_attn_merge(const Problem &pg, int idx_stride, float *out, const float *partials,
                              int32_t *bump_seq_len, hipStream_t st) {
+    const Problem p = attn_problem(pg);
     return launch_merge(p, attn_max_splits(p, idx_stride), out, partials, bump_seq_len, st);
 }
 

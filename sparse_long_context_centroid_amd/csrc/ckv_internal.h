@@ -13,13 +13,20 @@ namespace ckv {
 // Validated copy of ckv_dims with derived sizes.
 struct Problem {
     int B, Hq, Hkv, D, gpk, Cmax, S, dtype;
+    // attention only: consecutive graphs that read one index list (the layer
+    // graph's list serves the graphs of its Hkv KV heads)
+    int list_div = 1;
     // optional timing of the next launch: events bound to the kernel's own start
     // and end (hipExtLaunchKernelGGL), null for none
     hipEvent_t ev_start = nullptr, ev_stop = nullptr;
     int G() const { return Hq / Hkv; }
-    int NG() const { return B * Hkv * gpk; }
-    int heads_per_graph() const { return gpk == 1 ? G() : 1; }
-    int graphs_per_seq() const { return Hkv * gpk; }
+    // gpk = 0: one graph per layer (per sequence), shared by every head
+    bool layer() const { return gpk == 0; }
+    int NG() const { return layer() ? B : B * Hkv * gpk; }
+    int heads_per_graph() const { return layer() ? Hq : (gpk == 1 ? G() : 1); }
+    int graphs_per_seq() const { return layer() ? 1 : Hkv * gpk; }
+    // centroid row length: one d-slice per KV head for the layer graph
+    int cdim() const { return layer() ? Hkv * D : D; }
     int elem_bytes() const { return dtype == CKV_DT_BF16 ? 2 : 4; }
 };
 
@@ -48,7 +55,18 @@ inline int log2_pow2(int x) {
 inline Problem dense_problem(const Problem &p) {
     Problem d = p;
     d.gpk = 1;
+    d.list_div = 1;
     return d;
+}
+// Attention runs per (sequence, KV head) with that head's G query heads; the
+// layer graph's one index list is read by all Hkv of them.
+inline Problem attn_problem(const Problem &p) {
+    Problem a = p;
+    if (p.layer()) {
+        a.gpk = 1;
+        a.list_div = p.Hkv;
+    }
+    return a;
 }
 inline int dense_max_splits(const Problem &p, const ckv_kv &kv, int *cpw) {
     const int ch = attn_chunk(p.D, p.elem_bytes());
@@ -66,7 +84,8 @@ inline size_t dense_partial_floats(const Problem &p, const ckv_kv &kv) {
 }
 
 // Workspace of the attention call: partials NG * GH * max_splits * (D + 2) fp32.
-inline size_t attn_partial_floats(const Problem &p, int index_stride) {
+inline size_t attn_partial_floats(const Problem &pg, int index_stride) {
+    const Problem p = attn_problem(pg);
     return (size_t)p.NG() * p.heads_per_graph() * attn_max_splits(p, index_stride) * (p.D + 2);
 }
 
@@ -108,6 +127,12 @@ hipError_t launch_drift(const Problem &p, const ckv_graphs &gr, const float *ref
 int edge_queries_per_block(const Problem &p);
 hipError_t launch_edges(const Problem &p, const void *q, const void *k, int n, float scale,
                         int topk, int32_t *idx, float *score, int32_t *pairs, hipStream_t st);
+// The layer graph's update (one workgroup per sequence); bump: seq_len += 1.
+bool layer_update_fits(const Problem &p, int n_cand);
+hipError_t launch_layer_update(const Problem &p, const void *k_new, const void *v_new,
+                               const int32_t *cand, int n_cand, const ckv_graphs &gr,
+                               const ckv_kv &kv, int32_t *assigned, int32_t *err, bool bump,
+                               hipStream_t st);
 hipError_t launch_update(const Problem &p, const void *k_new, const void *v_new,
                          const int32_t *cand, int n_cand, const ckv_graphs &gr, const ckv_kv &kv,
                          int32_t *assigned, int32_t *err, hipStream_t st);

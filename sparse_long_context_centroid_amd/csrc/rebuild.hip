@@ -31,16 +31,19 @@ __global__ __launch_bounds__(kRebuildWaves * kWave) void rebuild_kernel(
     const int32_t *__restrict__ comm_start, const int32_t *__restrict__ comm_size,
     const int32_t *__restrict__ members, int Cmax, int Hkv, int gpk, float *__restrict__ out,
     int32_t *__restrict__ err) {
+    // blockIdx.y is the centroid set: the graph itself, or for the layer graph
+    // (gpk = 0) one KV head's slice of the sequence's graph (set = b*Hkv + kvh)
     constexpr int E = D / kWave;  // elements per lane
     static_assert(E >= 1 && D % kWave == 0, "row split");
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
-    const int g = blockIdx.y;
+    const int set = blockIdx.y;
+    const int g = gpk == 0 ? set / Hkv : set;  // graph of the community arrays
     const int c = blockIdx.x * kRebuildWaves + w;
     const int C = min(num_comms[g], Cmax);
     if (c >= C) return;
-    const int b = g / (Hkv * gpk);
-    const int kvh = (g / gpk) % Hkv;
+    const int b = gpk == 0 ? g : g / (Hkv * gpk);
+    const int kvh = gpk == 0 ? set % Hkv : (g / gpk) % Hkv;
     const int n = seq_len[b];
     const int sz = comm_size[(size_t)g * Cmax + c];
     const int st = comm_start[(size_t)g * Cmax + c];
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(kRebuildWaves * kWave) void rebuild_kernel(
         }
     }
     if (__ballot(bad) && lane == 0) set_err(err, CKV_DEVERR_INDEX_RANGE);
-    float *og = out + (size_t)g * (D / 4) * Cmax * 4;
+    float *og = out + (size_t)set * (D / 4) * Cmax * 4;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int i = lane * E + e;
@@ -95,23 +98,24 @@ __global__ __launch_bounds__(kRebuildWaves * kWave) void rebuild_kernel(
 // community-interleaved layout lane c reads community c, so every wave-wide load is
 // one contiguous 1 KiB line and no cross-lane sum is needed.
 constexpr int kDriftThreads = 256;
-template <int D>
+// d4: float4 chunks of a centroid row (d/4, or Hkv*d/4 for the layer graph), a
+// multiple of KC
 __global__ __launch_bounds__(kDriftThreads) void drift_kernel(
     const float *__restrict__ cent, const float *__restrict__ ref,
     const int32_t *__restrict__ num_comms, const int32_t *__restrict__ comm_size, int Cmax,
-    float *__restrict__ drift) {
+    int d4, float *__restrict__ drift) {
     constexpr int KC = 8;  // float4 chunks in flight per operand
     __shared__ double s_worst[kDriftThreads / kWave];
     const int g = blockIdx.x;
     const int C = min(num_comms[g], Cmax);
-    const float4 *cg = reinterpret_cast<const float4 *>(cent) + (size_t)g * (D / 4) * Cmax;
-    const float4 *rg = reinterpret_cast<const float4 *>(ref) + (size_t)g * (D / 4) * Cmax;
+    const float4 *cg = reinterpret_cast<const float4 *>(cent) + (size_t)g * d4 * Cmax;
+    const float4 *rg = reinterpret_cast<const float4 *>(ref) + (size_t)g * d4 * Cmax;
     double worst = 0.0;
     for (int c = threadIdx.x; c < C; c += kDriftThreads) {
         if (comm_size[(size_t)g * Cmax + c] <= 0) continue;
         double num = 0.0, den = 0.0;
 #pragma unroll 1
-        for (int k0 = 0; k0 < D / 4; k0 += KC) {
+        for (int k0 = 0; k0 < d4; k0 += KC) {
             float4 a[KC], r[KC];
 #pragma unroll
             for (int k = 0; k < KC; ++k) {
@@ -149,7 +153,8 @@ __global__ __launch_bounds__(kDriftThreads) void drift_kernel(
 
 hipError_t launch_rebuild(const Problem &p, const ckv_graphs &gr, const ckv_kv &kv, float *out,
                           int32_t *err, hipStream_t st) {
-    const dim3 grid((p.Cmax + kRebuildWaves - 1) / kRebuildWaves, p.NG());
+    const dim3 grid((p.Cmax + kRebuildWaves - 1) / kRebuildWaves,
+                    p.layer() ? p.B * p.Hkv : p.NG());
 #define CKV_REBUILD_CASE(TT, DT, DD)                                                           \
     if (p.dtype == DT && p.D == DD) {                                                          \
         hipExtLaunchKernelGGL((rebuild_kernel<TT, DD>), grid, dim3(kRebuildWaves * kWave), 0,  \
@@ -167,16 +172,10 @@ hipError_t launch_rebuild(const Problem &p, const ckv_graphs &gr, const ckv_kv &
 
 hipError_t launch_drift(const Problem &p, const ckv_graphs &gr, const float *ref, float *drift,
                         hipStream_t st) {
-    if (p.D == 128)
-        hipExtLaunchKernelGGL((drift_kernel<128>), dim3(p.NG()), dim3(kDriftThreads), 0,
-                              st, p.ev_start, p.ev_stop, 0, gr.centroids, ref, gr.num_comms,
-                              gr.comm_size, p.Cmax, drift);
-    else if (p.D == 64)
-        hipExtLaunchKernelGGL((drift_kernel<64>), dim3(p.NG()), dim3(kDriftThreads), 0,
-                              st, p.ev_start, p.ev_stop, 0, gr.centroids, ref, gr.num_comms,
-                              gr.comm_size, p.Cmax, drift);
-    else
-        return hipErrorInvalidValue;
+    if ((p.cdim() / 4) % 8 != 0) return hipErrorInvalidValue;
+    hipExtLaunchKernelGGL(drift_kernel, dim3(p.NG()), dim3(kDriftThreads), 0, st, p.ev_start,
+                          p.ev_stop, 0, gr.centroids, ref, gr.num_comms, gr.comm_size, p.Cmax,
+                          p.cdim() / 4, drift);
     return hipGetLastError();
 }
 

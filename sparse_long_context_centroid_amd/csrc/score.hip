@@ -121,6 +121,102 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     if (c0 < C) scores[(size_t)g * Cmax + c] = sz > 0 ? (float)(best * scale) : -__builtin_inff();
 }
 
+// The layer graph (one graph per sequence b, shared by every head; same post,
+// granularity section): a community carries one centroid per KV head, and its
+// score is the max over every query head h of q_h . mu_{c, kv head of h}:
+//   s[b][c] = max over KV heads k of fp32( max_{h in group k} (q_h . mu_{b,k,c}) * scale ).
+// The centroid of (b, k) is set b*Hkv + k of the interleaved layout.  The same
+// lane-per-community stream as above, once per KV head, with that head's G
+// queries restaged in LDS.
+template <typename T, int D, int GH>
+__global__ __launch_bounds__(kScoreThreads) void layer_score_kernel(
+    const T *__restrict__ q, const float *__restrict__ cent, const int32_t *__restrict__ num_comms,
+    const int32_t *__restrict__ comm_size, int Cmax, int Hq, int Hkv, double scale,
+    float *__restrict__ scores) {
+    constexpr int KC = kScoreChunk;
+    static_assert((D / 4) % KC == 0, "whole chunks");
+    constexpr int NQ = (D * GH / 4 + kScoreThreads - 1) / kScoreThreads;
+    __shared__ double sq[NQ * kScoreThreads * 4];
+    const int b = blockIdx.y;
+    const int c0 = blockIdx.x * kScoreThreads + threadIdx.x;
+    const int c = min(c0, Cmax - 1);
+    const int sz = comm_size[(size_t)b * Cmax + c];
+    const int C = min(num_comms[b], Cmax);
+    if ((int)(blockIdx.x * kScoreThreads) >= C) return;
+    using Q4 = typename std::conditional<sizeof(T) == 2, uint2, float4>::type;
+    float best = -__builtin_inff();
+#pragma unroll 1
+    for (int kvh = 0; kvh < Hkv; ++kvh) {
+        const int h0 = kvh * GH;
+        Q4 qraw[NQ];
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const int jq = min((int)threadIdx.x + j * kScoreThreads, D * GH / 4 - 1);
+            qraw[j] = *reinterpret_cast<const Q4 *>(q + ((size_t)b * Hq + h0 + jq % GH) * D +
+                                                    (jq / GH) * 4);
+        }
+        const float4 *cp = reinterpret_cast<const float4 *>(cent) +
+                           ((size_t)b * Hkv + kvh) * (D / 4) * Cmax + c;
+        float4 cur[KC];
+#pragma unroll
+        for (int k = 0; k < KC; ++k) cur[k] = cp[(size_t)k * Cmax];
+        __syncthreads();  // the previous KV head's queries are no longer read
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            float e4[4];
+            if constexpr (sizeof(T) == 2) {
+                const uint2 w = reinterpret_cast<const uint2 &>(qraw[j]);
+                e4[0] = bf16_lo(w.x);
+                e4[1] = bf16_hi(w.x);
+                e4[2] = bf16_lo(w.y);
+                e4[3] = bf16_hi(w.y);
+            } else {
+                const float4 w = reinterpret_cast<const float4 &>(qraw[j]);
+                e4[0] = w.x;
+                e4[1] = w.y;
+                e4[2] = w.z;
+                e4[3] = w.w;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sq[(threadIdx.x + j * kScoreThreads) * 4 + e] = (double)e4[e];
+        }
+        __syncthreads();
+        double acc[GH];
+#pragma unroll
+        for (int h = 0; h < GH; ++h) acc[h] = 0.0;
+#pragma unroll 1
+        for (int k0 = 0; k0 < D / 4; k0 += KC) {
+            float4 nxt[KC];
+            const int kn = min(k0 + KC, D / 4 - KC);
+#pragma unroll
+            for (int k = 0; k < KC; ++k) nxt[k] = cp[(size_t)(kn + k) * Cmax];
+#pragma unroll
+            for (int kk = 0; kk < KC; ++kk) {
+                const int k = k0 + kk;
+                const double e0 = cur[kk].x, e1 = cur[kk].y, e2 = cur[kk].z, e3 = cur[kk].w;
+#pragma unroll
+                for (int h = 0; h < GH; ++h) {
+                    const double *qq = sq + (k * GH + h) * 4;
+                    acc[h] = fma(qq[0], e0, acc[h]);
+                    acc[h] = fma(qq[1], e1, acc[h]);
+                    acc[h] = fma(qq[2], e2, acc[h]);
+                    acc[h] = fma(qq[3], e3, acc[h]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < KC; ++k) cur[k] = nxt[k];
+        }
+        double m = acc[0];
+#pragma unroll
+        for (int h = 1; h < GH; ++h)
+            if (acc[h] > m) m = acc[h];
+        const float v = (float)(m * scale);
+        best = v > best ? v : best;
+    }
+    if (c0 < C) scores[(size_t)b * Cmax + c] = sz > 0 ? best : -__builtin_inff();
+}
+
 // ---- layout helpers ---------------------------------------------------------------
 __global__ void rows_to_interleaved_kernel(const float *__restrict__ rows, float *__restrict__ out,
                                            int NG, int Cmax, int D) {
@@ -157,8 +253,36 @@ static void launch_score_t(const Problem &p, const void *q, const ckv_graphs &gr
                        gr.num_comms, gr.comm_size, p.Cmax, p.Hq, p.Hkv, p.gpk, scale, scores);
 }
 
+template <typename T, int D, int GH>
+static void launch_layer_score_t(const Problem &p, const void *q, const ckv_graphs &gr,
+                                 double scale, float *scores, hipStream_t st) {
+    hipExtLaunchKernelGGL((layer_score_kernel<T, D, GH>),
+                          dim3((p.Cmax + kScoreThreads - 1) / kScoreThreads, p.B),
+                          dim3(kScoreThreads), 0, st, p.ev_start, p.ev_stop, 0,
+                          static_cast<const T *>(q), gr.centroids, gr.num_comms, gr.comm_size,
+                          p.Cmax, p.Hq, p.Hkv, scale, scores);
+}
+
 hipError_t launch_score(const Problem &p, const void *q, const ckv_graphs &gr, double scale,
                         float *scores, hipStream_t st) {
+    if (p.layer()) {
+        const int G = p.G();
+#define CKV_LSCORE_CASE(TT, DT, DD, HH)                                                        \
+        if (p.dtype == DT && p.D == DD && G == HH) {                                           \
+            launch_layer_score_t<TT, DD, HH>(p, q, gr, scale, scores, st);                     \
+            return hipGetLastError();                                                          \
+        }
+        CKV_LSCORE_CASE(bf16_t, CKV_DT_BF16, 128, 1) CKV_LSCORE_CASE(bf16_t, CKV_DT_BF16, 128, 2)
+        CKV_LSCORE_CASE(bf16_t, CKV_DT_BF16, 128, 4) CKV_LSCORE_CASE(bf16_t, CKV_DT_BF16, 128, 8)
+        CKV_LSCORE_CASE(bf16_t, CKV_DT_BF16, 64, 1) CKV_LSCORE_CASE(bf16_t, CKV_DT_BF16, 64, 2)
+        CKV_LSCORE_CASE(bf16_t, CKV_DT_BF16, 64, 4) CKV_LSCORE_CASE(bf16_t, CKV_DT_BF16, 64, 8)
+        CKV_LSCORE_CASE(float, CKV_DT_F32, 128, 1) CKV_LSCORE_CASE(float, CKV_DT_F32, 128, 2)
+        CKV_LSCORE_CASE(float, CKV_DT_F32, 128, 4) CKV_LSCORE_CASE(float, CKV_DT_F32, 128, 8)
+        CKV_LSCORE_CASE(float, CKV_DT_F32, 64, 1) CKV_LSCORE_CASE(float, CKV_DT_F32, 64, 2)
+        CKV_LSCORE_CASE(float, CKV_DT_F32, 64, 4) CKV_LSCORE_CASE(float, CKV_DT_F32, 64, 8)
+#undef CKV_LSCORE_CASE
+        return hipErrorInvalidValue;
+    }
     const int GH = p.heads_per_graph();
 #define CKV_SCORE_CASE(TT, DT, DD, HH)                                                         \
     if (p.dtype == DT && p.D == DD && GH == HH) {                                              \
@@ -180,14 +304,14 @@ hipError_t launch_score(const Problem &p, const void *q, const ckv_graphs &gr, d
 hipError_t launch_rows_to_interleaved(const Problem &p, const float *rows, float *cent,
                                       hipStream_t st) {
     hipLaunchKernelGGL(rows_to_interleaved_kernel, dim3(1024), dim3(256), 0, st, rows, cent,
-                       p.NG(), p.Cmax, p.D);
+                       p.NG(), p.Cmax, p.cdim());
     return hipGetLastError();
 }
 
 hipError_t launch_interleaved_to_rows(const Problem &p, const float *cent, float *rows,
                                       hipStream_t st) {
     hipLaunchKernelGGL(interleaved_to_rows_kernel, dim3(1024), dim3(256), 0, st, cent, rows,
-                       p.NG(), p.Cmax, p.D);
+                       p.NG(), p.Cmax, p.cdim());
     return hipGetLastError();
 }
 

@@ -43,9 +43,173 @@ static void launch_update_t(const Problem &p, const void *k_new, const void *v_n
                        kv.max_pages_per_seq, kv.num_pages, kv.seq_len, assigned, err);
 }
 
+// The layer graph: one graph per sequence b, whose centroid rows hold one d-slice
+// per KV head (E = Hkv*d values, KV head after KV head).  The new token's key row
+// is the concatenation of its Hkv keys; it joins the candidate whose row is
+// nearest in squared L2 over all E values (summed in fp64 in element order by the
+// candidate's lane; lower id on equal distance), that community's whole row moves
+// to the running mean, and K/V row n is written in every KV head.
+//
+// One workgroup per sequence: k_new is widened to fp64 in LDS and the candidates'
+// rows are staged there by the whole workgroup (every load in flight at once);
+// the first wave's lanes 0..M-1 then sum one distance each.  LDS: E doubles plus
+// M rows of E+4 floats (the host checks the size).
+constexpr int kLayerUpdThreads = 256;
+inline size_t layer_update_lds(int E, int M) {
+    return (size_t)E * sizeof(double) + (size_t)M * (E + 4) * sizeof(float);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kLayerUpdThreads) void layer_update_kernel(
+    const T *__restrict__ k_new, const T *__restrict__ v_new, const int32_t *__restrict__ cand,
+    int M, float *__restrict__ cent, const int32_t *__restrict__ num_comms,
+    const int32_t *__restrict__ comm_start, int32_t *__restrict__ comm_size,
+    const int32_t *__restrict__ comm_cap, int32_t *__restrict__ members, int Cmax, int Hkv,
+    T *__restrict__ kc, T *__restrict__ vc, const int32_t *__restrict__ page_table, int log2ps,
+    int max_pages, int num_pages, int32_t *__restrict__ seq_len, int bump,
+    int32_t *__restrict__ assigned, int32_t *__restrict__ err) {
+#pragma clang fp contract(off)
+    extern __shared__ __align__(16) unsigned char s_raw[];
+    __shared__ int s_best, s_slot, s_new;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int E = Hkv * D, E4 = E / 4, CS = E + 4;
+    double *kn64 = reinterpret_cast<double *>(s_raw);
+    float *lc = reinterpret_cast<float *>(kn64 + E);
+    const int n = seq_len[b];
+    const int C = min(num_comms[b], Cmax);
+    const T *kn = k_new + (size_t)b * E;
+    const T *vn = v_new + (size_t)b * E;
+    for (int i = tid; i < E; i += kLayerUpdThreads) kn64[i] = (double)to_f32(kn[i]);
+    // candidate rows: element 4*k4 .. +3 of community c at float4 (b*E4 + k4)*Cmax + c
+    const float4 *c4 = reinterpret_cast<const float4 *>(cent) + (size_t)b * E4 * Cmax;
+    for (int t = tid; t < M * E4; t += kLayerUpdThreads) {
+        const int sl = t / E4, k4 = t % E4;
+        const int cc = cand[(size_t)b * M + sl];
+        const int cl = (cc >= 0 && cc < C) ? cc : 0;
+        *reinterpret_cast<float4 *>(lc + sl * CS + 4 * k4) = c4[(size_t)k4 * Cmax + cl];
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        const int lane = tid;
+        const int cc = lane < M ? cand[(size_t)b * M + lane] : -1;
+        const int c = (cc >= 0 && cc < C) ? cc : -1;
+        double dist = __builtin_inf();
+        if (c >= 0) {
+            double s = 0.0;
+            const float *mu = lc + lane * CS;
+            for (int i = 0; i < E; ++i) {
+                const double diff = kn64[i] - (double)mu[i];
+                const double sq = diff * diff;
+                s = s + sq;
+            }
+            dist = s;
+        }
+        int best = c, slot = c >= 0 ? lane : -1;
+        double bd = dist;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const double od = __shfl_xor(bd, off);
+            const int oc = __shfl_xor(best, off);
+            const int os = __shfl_xor(slot, off);
+            if (oc >= 0 && (best < 0 || od < bd || (od == bd && oc < best))) {
+                bd = od;
+                best = oc;
+                slot = os;
+            }
+        }
+        if (lane == 0) {
+            int slot_new = -1;
+            if (best >= 0) {
+                const size_t gc = (size_t)b * Cmax + best;
+                const int sz = comm_size[gc];
+                if (sz < comm_cap[gc]) {
+                    members[(size_t)comm_start[gc] + sz] = n;
+                    comm_size[gc] = sz + 1;
+                    slot_new = sz;
+                } else {
+                    set_err(err, CKV_DEVERR_CAPACITY);
+                }
+            }
+            assigned[b] = slot_new >= 0 ? best : -1;
+            s_best = best;
+            s_slot = slot;
+            s_new = slot_new;
+        }
+    }
+    __syncthreads();
+    const int best = s_best, slot_new = s_new;
+    if (slot_new >= 0) {
+        // running mean of the winner's whole row, from its LDS copy
+        const double cnt = (double)(slot_new + 1);
+        const float *mu = lc + s_slot * CS;
+        for (int i = tid; i < E; i += kLayerUpdThreads) {
+            const double m0 = (double)mu[i];
+            const double step = (kn64[i] - m0) / cnt;
+            cent[(((size_t)b * E4 + i / 4) * Cmax + best) * 4 + i % 4] = (float)(m0 + step);
+        }
+    }
+    // K/V row n in every KV head
+    const int lp = n >> log2ps;
+    const int pg = lp < max_pages ? page_table[(size_t)b * max_pages + lp] : -1;
+    if (pg >= 0 && pg < num_pages) {
+        for (int i = tid; i < E; i += kLayerUpdThreads) {
+            const int kvh = i / D, e = i % D;
+            const size_t row =
+                (((size_t)pg * Hkv + kvh) << log2ps) + (n & ((1 << log2ps) - 1));
+            kc[row * D + e] = kn[i];
+            vc[row * D + e] = vn[i];
+        }
+    } else if (tid == 0) {
+        set_err(err, CKV_DEVERR_UNMAPPED_PAGE);
+    }
+    if (bump) {
+        __syncthreads();
+        if (tid == 0) seq_len[b] = n + 1;
+    }
+}
+
+template <typename T, int D>
+static void launch_layer_update_t(const Problem &p, const void *k_new, const void *v_new,
+                                  const int32_t *cand, int M, const ckv_graphs &gr,
+                                  const ckv_kv &kv, int32_t *assigned, int32_t *err, bool bump,
+                                  hipStream_t st) {
+    hipLaunchKernelGGL((layer_update_kernel<T, D>), dim3(p.B), dim3(kLayerUpdThreads),
+                       layer_update_lds(p.cdim(), M), st, static_cast<const T *>(k_new),
+                       static_cast<const T *>(v_new), cand, M, gr.centroids, gr.num_comms,
+                       gr.comm_start, gr.comm_size, gr.comm_cap, gr.members, p.Cmax, p.Hkv,
+                       static_cast<T *>(kv.k), static_cast<T *>(kv.v), kv.page_table,
+                       log2_pow2(kv.page_size), kv.max_pages_per_seq, kv.num_pages, kv.seq_len,
+                       bump ? 1 : 0, assigned, err);
+}
+
+bool layer_update_fits(const Problem &p, int n_cand) {
+    return layer_update_lds(p.cdim(), n_cand) <= 65536;
+}
+
+hipError_t launch_layer_update(const Problem &p, const void *k_new, const void *v_new,
+                               const int32_t *cand, int n_cand, const ckv_graphs &gr,
+                               const ckv_kv &kv, int32_t *assigned, int32_t *err, bool bump,
+                               hipStream_t st) {
+    if (!layer_update_fits(p, n_cand)) return hipErrorInvalidValue;
+#define CKV_LUPD_CASE(TT, DT, DD)                                                              \
+    if (p.dtype == DT && p.D == DD) {                                                          \
+        launch_layer_update_t<TT, DD>(p, k_new, v_new, cand, n_cand, gr, kv, assigned, err,    \
+                                      bump, st);                                               \
+        return hipGetLastError();                                                              \
+    }
+    CKV_LUPD_CASE(bf16_t, CKV_DT_BF16, 128) CKV_LUPD_CASE(bf16_t, CKV_DT_BF16, 64)
+    CKV_LUPD_CASE(float, CKV_DT_F32, 128) CKV_LUPD_CASE(float, CKV_DT_F32, 64)
+#undef CKV_LUPD_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_update(const Problem &p, const void *k_new, const void *v_new,
                          const int32_t *cand, int n_cand, const ckv_graphs &gr, const ckv_kv &kv,
                          int32_t *assigned, int32_t *err, hipStream_t st) {
+    if (p.layer())
+        return launch_layer_update(p, k_new, v_new, cand, n_cand, gr, kv, assigned, err, true,
+                                   st);
 #define CKV_UPD_CASE(TT, DT, DD)                                                               \
     if (p.dtype == DT && p.D == DD) {                                                          \
         launch_update_t<TT, DD>(p, k_new, v_new, cand, n_cand, gr, kv, assigned, err, st);     \

@@ -139,6 +139,25 @@ def test_prefill_edges_validate(lib):
                                  None) == -2
 
 
+def test_layer_graph_dims(lib):
+    """graphs_per_kv = 0 (one graph per layer): the attention workspace is the group
+    graph's (the one list feeds every KV head's G query heads); the update refuses
+    candidate rows that do not fit its LDS stage; the prefill edges refuse it."""
+    lay, grp = dims(B=4, gpk=0), dims(B=4, gpk=1)
+    assert lib.ckv_workspace_size(C.byref(lay), 4100) == lib.ckv_workspace_size(C.byref(grp), 4100)
+    fake = C.c_void_p(0x1000)
+    g = Bd.ckv_graphs(fake, fake, fake, fake, fake, fake)
+    kv = Bd.ckv_kv(fake, fake, fake, 16, 8, 8, fake)
+    # 8 KV heads x d 128: 16 candidate rows of 1028 floats + 1024 doubles > 64 KiB
+    assert lib.ckv_local_update(C.byref(lay), fake, fake, fake, 16, C.byref(g), C.byref(kv),
+                                fake, fake, None) == -2
+    assert lib.ckv_decode_step(C.byref(lay), fake, fake, fake, C.byref(g), C.byref(kv), fake, 16,
+                               0.1, fake, fake, 2052, fake, None, fake, None, fake, fake, fake,
+                               1 << 30, fake, None, None) == -2
+    assert lib.ckv_prefill_edges(C.byref(lay), fake, fake, 64, 8, 0.1, fake, fake, None, None,
+                                 None) == -2
+
+
 def test_status_strings(lib):
     for s, txt in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported configuration"),
                    (-3, "workspace missing or too small"), (-4, "HIP launch failed")]:
