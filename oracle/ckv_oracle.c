@@ -250,6 +250,53 @@ int ckvo_update(int d, const void *k_new, int dtype, const int32_t *cand, int n_
 }
 
 /*
+ * The update of a whole-layer graph [RIT-granul, RIT-plan: one graph may serve a
+ * whole layer].  A centroid row is nseg slices of d values, one slice per KV head
+ * (row length nseg*d), and k_new is the matching row of the new token's keys.
+ * Reading: the distance of a candidate is the squared L2 distance over the row,
+ * accumulated per KV head -- each slice's sum in fp64 in element order, then the
+ * slices' sums added in slice order; lower id on equal distance.  The winner's
+ * whole row moves to the running mean, exactly as in ckvo_update.
+ */
+int ckvo_update_layer(int d, int nseg, const void *k_new, int dtype, const int32_t *cand,
+                      int n_cand, float *cent, int32_t *size, const int32_t *cap,
+                      const int32_t *start, int32_t *members, int n)
+{
+    const long row = (long)d * nseg;
+    int win = -1;
+    double win_dist = INFINITY;
+    for (int m = 0; m < n_cand; ++m) {
+        const int c = cand[m];
+        double total = 0.0;
+        for (int sg = 0; sg < nseg; ++sg) {
+            double part = 0.0;
+            for (int i = 0; i < d; ++i) {
+                long e = (long)sg * d + i;
+                const double gap = widen(k_new, e, dtype) - (double)cent[(long)c * row + e];
+                part = part + gap * gap;
+            }
+            total = total + part;
+        }
+        if (total < win_dist || (total == win_dist && c < win)) {
+            win_dist = total;
+            win = c;
+        }
+    }
+    if (win < 0)
+        return -2;
+    if (size[win] >= cap[win])
+        return -1;
+    members[start[win] + size[win]] = n;
+    size[win] += 1;
+    const double count = (double)size[win];
+    for (long e = 0; e < row; ++e) {
+        const double old_mu = (double)cent[(long)win * row + e];
+        cent[(long)win * row + e] = (float)(old_mu + (widen(k_new, e, dtype) - old_mu) / count);
+    }
+    return win;
+}
+
+/*
  * Centroid of every community recomputed from its member list: the plain mean of
  * the member keys [RIT-graph: each community has a centre; RIT-plan: local
  * assignments drift over long generations, and the partition is refreshed from
@@ -326,8 +373,7 @@ void ckvo_edge_scores(int d, int G, const void *Q, const void *K, int dtype, flo
             double dot = 0.0;
             for (int e = 0; e < d; ++e)
                 dot = dot + widen(Q, (i * G + h) * d + e, dtype) * widen(K, j * d + e, dtype);
-            if (dot > best)
-                best = dot;
+            best = dot > best ? dot : best;
         }
         z[r] = best * (double)scale;
     }

@@ -23,7 +23,9 @@ mean of its members' keys in that head), stored as one row of Hkv*d values,
 KV head after KV head; its score is the max over all query heads of
 q_h . mu_{c, kv head of h} * scale (the group reading, over the whole layer);
 one index list serves every KV head; the new token joins the nearest candidate
-in squared L2 over the whole row (all KV heads' keys, in that order).
+in squared L2 over the whole row (all KV heads' keys), accumulated per KV head:
+each head's slice summed in element order, then the slices in head order
+(ckvo_update_layer).
 """
 from __future__ import annotations
 
@@ -87,6 +89,8 @@ def lib():
             L.ckvo_edges.restype = None
             L.ckvo_edge_scores.argtypes = [i32, i32, P, P, i32, C.c_float, P, P, i32, P]
             L.ckvo_edge_scores.restype = None
+            L.ckvo_update_layer.argtypes = [i32, i32, P, i32, P, i32, P, P, P, P, P, i32]
+            L.ckvo_update_layer.restype = i32
             _lib = L
     return _lib
 
@@ -212,6 +216,23 @@ def edges(Q: np.ndarray, K: np.ndarray, S: int, scale: float, topk: int, rows=No
     return idx, score
 
 
+def update_layer(k_new: np.ndarray, cand: np.ndarray, cent: np.ndarray, size: np.ndarray,
+                 cap: np.ndarray, start: np.ndarray, members: np.ndarray, n: int, nseg: int):
+    """The layer graph's update: rows of nseg slices (one per KV head); in place
+    like update().  -> chosen id or <0."""
+    for a in (cent, size, members):
+        assert a.flags["C_CONTIGUOUS"] and a.flags["WRITEABLE"]
+    cand = np.ascontiguousarray(cand, np.int32)
+    cap = np.ascontiguousarray(cap, np.int32)
+    start = np.ascontiguousarray(start, np.int32)
+    k_new = np.ascontiguousarray(k_new)
+    row = cent.shape[1]
+    assert row % nseg == 0 and k_new.size == row
+    return lib().ckvo_update_layer(row // nseg, nseg, _p(k_new), _dt(k_new), _p(cand),
+                                   cand.shape[0], _p(cent), _p(size), _p(cap), _p(start),
+                                   _p(members), int(n))
+
+
 def edge_scores(Q: np.ndarray, K: np.ndarray, scale: float, rows, keys) -> np.ndarray:
     """fp64 group scores z of (query rows[r], key keys[r]) pairs, as in edges()."""
     Q = np.ascontiguousarray(Q)
@@ -280,9 +301,9 @@ class OracleState:
         for kvh in range(self.Hkv):
             for h in range(kvh * G, (kvh + 1) * G):
                 outs[h] = attend(q[b, h], self.K[b, kvh], self.V[b, kvh], idx, scale)
-        r, _ = update(np.ascontiguousarray(k_new[b]).reshape(-1), cand, self.cent[g, :Cn],
-                      self.size[g, :Cn], self.cap[g, :Cn], self.start[g, :Cn], self.members,
-                      n) if Cn else (-2, 0)
+        r = update_layer(np.ascontiguousarray(k_new[b]).reshape(-1), cand, self.cent[g, :Cn],
+                         self.size[g, :Cn], self.cap[g, :Cn], self.start[g, :Cn],
+                         self.members, n, self.Hkv) if Cn else -2
         res[g] = (s, sel, k, cand, idx, outs, r)
 
     def _graph_step(self, g, q, k_new, budget, scale, M, max_len, res):

@@ -62,8 +62,11 @@ MUTANTS = {
                         "            continue;\n"
                         "        double *z = (double *)malloc(sizeof(double) * (size_t)cnt);\n"
                         "        for (int j = lo; j <= i; ++j) {"),
-    "edge-scores-min-of-heads": ("            if (dot > best)\n                best = dot;\n        }\n        z[r]",
-                                 "            if (h == 0 || dot < best)\n                best = dot;\n        }\n        z[r]"),
+    "edge-scores-min-of-heads": ("best = dot > best ? dot : best;",
+                                 "best = (h == 0 || dot < best) ? dot : best;"),
+    "layer-update-skips-last-slice": ("for (int sg = 0; sg < nseg; ++sg) {",
+                                      "for (int sg = 0; sg < nseg - 1; ++sg) {"),
+    "layer-update-slice-offset": ("long e = (long)sg * d + i;", "long e = i;"),
     "edges-include-sinks": ("int lo = S;\n        int cnt", "int lo = 0;\n        int cnt"),
     "edges-tie-high-position": ("(arg < 0 || z[j] > z[arg])", "(arg < 0 || z[j] >= z[arg])"),
     "drift-not-relative": ("double r = den > 0.0 ? sqrt(num) / sqrt(den) : sqrt(num);",

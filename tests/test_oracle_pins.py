@@ -677,3 +677,47 @@ def test_layer_graph_score_is_max_over_all_heads_of_their_own_head_slice():
     fin = np.isfinite(want)
     assert np.array_equal(np.isfinite(got), fin)
     assert np.allclose(got[fin], want[fin], rtol=2e-7, atol=1e-6)
+
+
+def test_layer_update_with_one_slice_is_the_group_update():
+    r = rng(41)
+    d, C, n = 24, 9, 500
+    for trial in range(20):
+        cent = r.standard_normal((C, d)).astype(np.float32)
+        kn = r.standard_normal(d).astype(np.float32)
+        size = r.integers(1, 5, C).astype(np.int32)
+        cap = size + 2
+        start = np.concatenate([[0], np.cumsum(cap)[:-1]]).astype(np.int32)
+        members = np.full(int(cap.sum()), -1, np.int32)
+        cand = r.permutation(C)[:6].astype(np.int32)
+        c1, s1, m1 = cent.copy(), size.copy(), members.copy()
+        c2, s2, m2 = cent.copy(), size.copy(), members.copy()
+        a, _ = O.update(kn, cand, c1, s1, cap, start, m1, n)
+        b = O.update_layer(kn, cand, c2, s2, cap, start, m2, n, 1)
+        assert a == b and np.array_equal(c1, c2) and np.array_equal(s1, s2)
+        assert np.array_equal(m1, m2)
+
+
+def test_layer_update_picks_the_nearest_whole_row():
+    """Brute force (longdouble) over rows of 3 slices: candidates that differ from
+    the new key in one slice only, so every slice must count."""
+    r = rng(42)
+    d, nseg, C = 4, 3, 6
+    row = d * nseg
+    for trial in range(60):
+        kn = r.standard_normal(row).astype(np.float32)
+        cent = np.repeat(kn[None], C, axis=0).astype(np.float32)
+        for c in range(C):
+            sl = r.integers(nseg)
+            cent[c, sl * d:(sl + 1) * d] += r.standard_normal(d).astype(np.float32)
+        size = np.ones(C, np.int32)
+        cap = np.full(C, 4, np.int32)
+        start = (np.arange(C) * 4).astype(np.int32)
+        members = np.full(4 * C, -1, np.int32)
+        cand = r.permutation(C).astype(np.int32)
+        dl = ((cent.astype(brute.LD) - kn.astype(brute.LD)) ** 2).sum(1)
+        want = int(np.argmin(dl))
+        assert np.sort(dl)[1] - dl[want] > 1e-6        # no near tie
+        got = O.update_layer(kn, cand, cent, size, cap, start, members, 77, nseg)
+        assert got == want, (trial, got, want)
+        assert size[want] == 2 and members[start[want] + 1] == 77
