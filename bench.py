@@ -49,9 +49,10 @@ def step_bytes(layer: Bd.DecodeLayer, idx_len: np.ndarray, elem: int):
     per-head graphs the union of the rows of a KV head's lists -- q and out, the
     candidate centroids and the appended row); workspace partials not counted."""
     d = layer.d
+    cd = layer.cdim                       # centroid row: d, or Hkv*d for the layer graph
     C = int(layer.num_comms_host.sum())
     Bq = layer.B * layer.Hq * d * elem
-    score = C * (d * 4 + 4 + 4) + Bq
+    score = C * (cd * 4 + 4 + 4) + Bq
     ntok = int(idx_len.sum())
     select = C * (4 + 4) + ntok * (4 + 4)
     if layer.gpk > 1:
@@ -60,10 +61,13 @@ def step_bytes(layer: Bd.DecodeLayer, idx_len: np.ndarray, elem: int):
         for kv in range(layer.B * layer.Hkv):
             gs = range(kv * layer.gpk, (kv + 1) * layer.gpk)
             rows += len(np.unique(np.concatenate([lists[g, :idx_len[g]] for g in gs])))
+        entries = ntok
+    elif layer.gpk == 0:
+        rows = entries = ntok * layer.Hkv  # every KV head reads the layer's one list
     else:
-        rows = ntok
-    attn = rows * 2 * d * elem + ntok * 4 + Bq
-    upd = layer.NG * (layer.M * d * 4 + layer.M * 4 + d * 4 * 2) + \
+        rows = entries = ntok
+    attn = rows * 2 * d * elem + entries * 4 + Bq
+    upd = layer.NG * (layer.M * cd * 4 + layer.M * 4 + cd * 4 * 2) + \
         layer.B * layer.Hkv * 2 * d * elem * 2
     merge = layer.B * layer.Hq * d * 4
     return dict(score=score, select=select, attn_update=attn + upd, merge=merge), attn
@@ -208,6 +212,82 @@ def edges_timing(wl, args):
                 prefill_tokens_per_s=n / (mean / 1e3))
 
 
+def graph_bytes(L, cdim: int) -> dict:
+    """Memory the graphs of one layer keep beside the KV cache: centroids as
+    allocated (Cmax padding) and as used (communities in use), the member pool
+    (with its append slack), and the three per-community int32 arrays."""
+    NG, Cmax = L.comm_start.shape
+    C = int(np.asarray(L.num_comms).sum())
+    cent_alloc = NG * Cmax * cdim * 4
+    cent_used = C * cdim * 4
+    members = int(L.members.size) * 4
+    percomm_alloc = 3 * NG * Cmax * 4
+    return dict(graphs=NG, communities=C, centroid_bytes=cent_alloc,
+                centroid_bytes_used=cent_used, member_bytes=members,
+                per_community_bytes=percomm_alloc,
+                total=cent_alloc + members + percomm_alloc,
+                total_used=cent_used + members + 3 * C * 4)
+
+
+def granularity_sweep(spec, args, scrub, elem):
+    """The same workload (layer 0) with one graph per KV head (group), per query
+    head, and per layer: step time under the cold protocol, the speed-up over dense
+    attention on the same cache, and the graphs' memory next to the KV cache."""
+    dev = "cuda:0"
+    K = max(3, min(args.steps, 20))
+    W = 3
+    out = []
+    dense_ms = None
+    for mode in ("group", "head", "layer"):
+        sp = I.granularity_spec(spec, mode)
+        wl = I.make_workload(sp, args.seed, device=dev, steps=W + K, layers=1)
+        lay = build_layers(wl, int(wl.S + wl.budget.max()))[0]
+        tm = Timed(lay)
+        L = wl.layers[0]
+        ms = []
+        for t in range(W + K):
+            if not args.warm:
+                scrub_sum = scrub.sum()
+            tm.run(L.q[t], L.k_new[t], L.v_new[t], wl.scale, per_kernel=False)
+            torch.cuda.synchronize()
+            if t >= W:
+                ms.append(tm.step_ms())
+        if int(lay.err.item()):
+            raise SystemExit(f"device error flag during the {mode} sweep")
+        if dense_ms is None:
+            # dense attention reads every cached token: the same for every granularity
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            dm = []
+            o = torch.empty_like(lay.out)
+            for t in range(5):
+                if not args.warm:
+                    scrub_sum = scrub.sum()
+                ev[0].record()
+                lay.dense(L.q[W + K - 1], wl.scale, out=o)
+                ev[1].record()
+                torch.cuda.synchronize()
+                if t >= 2:
+                    dm.append(ev[0].elapsed_time(ev[1]))
+            dense_ms = float(np.mean(dm))
+        n = wl.seq_len0.astype(np.float64)
+        kv_bytes = float(n.sum()) * wl.Hkv * 2 * wl.d * elem
+        gb = graph_bytes(L, wl.Hkv * wl.d if wl.gpk == 0 else wl.d)
+        step = float(np.mean(ms))
+        out.append(dict(graphs=mode, workload=sp.name, graphs_per_layer=gb["graphs"],
+                        ms_per_step=step, tokens_per_s=wl.B / (step / 1e3),
+                        speedup_vs_dense=dense_ms / step, dense_ms_per_step=dense_ms,
+                        mean_index_len=float(lay.index_len.float().mean().item()),
+                        graph_bytes=gb, kv_bytes=kv_bytes,
+                        graph_overhead_vs_kv=gb["total"] / kv_bytes,
+                        graph_overhead_vs_kv_used=gb["total_used"] / kv_bytes))
+        log(f"[bench] granularity {mode}: {step * 1e3:.1f} us/step, "
+            f"{dense_ms / step:.2f}x dense, graphs {gb['total'] / 1e6:.1f} MB = "
+            f"{100 * gb['total'] / kv_bytes:.2f}% of KV")
+        del lay, tm, wl, L
+        torch.cuda.empty_cache()
+    return out
+
+
 def build_layers(wl, index_stride):
     layers = []
     for li in range(len(wl.layers)):
@@ -246,6 +326,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--graphs", choices=("config", "group", "head", "layer"), default="config",
+                    help="graph granularity of the timed workload (default: the config's own)")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -255,6 +337,8 @@ def main():
                     help="skip timing the centroid rebuild from the member lists")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-attention baseline (every cached token)")
+    ap.add_argument("--no-granularity", action="store_true",
+                    help="skip the graph-granularity sweep (group / per-head / per-layer)")
     ap.add_argument("--no-edges", action="store_true",
                     help="skip the prefill edge-extraction measurement")
     ap.add_argument("--seed", type=int, default=None)
@@ -274,8 +358,10 @@ def main():
     # events (roofline); the per-kernel events are kept out of the value pass
     T = args.warmup + 2 * args.steps
     spec = I.CONFIGS[args.config]
+    if args.graphs != "config":
+        spec = I.granularity_spec(spec, args.graphs)
     t0 = time.perf_counter()
-    wl = I.make_workload(args.config, args.seed, device=dev, steps=T, layers=args.layers)
+    wl = I.make_workload(spec, args.seed, device=dev, steps=T, layers=args.layers)
     torch.cuda.synchronize()
     log(f"[bench] workload {spec.name}: {len(wl.layers)} layer(s), B={wl.B}, "
         f"n={wl.seq_len0.tolist()[:4]}..., Cmax={wl.Cmax}, generated in "
@@ -338,6 +424,9 @@ def main():
     dense = None
     if not args.no_dense:
         dense = dense_baseline(layers, qkv, wl, scrub, args, elem)
+    sweep = None
+    if not args.no_granularity:
+        sweep = granularity_sweep(spec, args, scrub, elem)
     edges = None
     if not args.no_edges:
         edges = edges_timing(wl, args)
@@ -372,7 +461,7 @@ def main():
             "workload": spec.name, "batch": wl.B, "layers": len(wl.layers),
             "context": int(wl.seq_len0.max()) if not spec.ragged else "8K-128K ragged",
             "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d,
-            "graphs": "per-head" if wl.gpk > 1 else "query-group",
+            "graphs": "per-head" if wl.gpk > 1 else ("per-layer" if wl.gpk == 0 else "query-group"),
             "budget": int(wl.budget.max()) if not spec.ragged else "5% of context",
             "sinks": wl.S, "n_cand": wl.M, "kv_dtype": "bf16" if elem == 2 else "fp32",
             "score_arith": "fp64", "attn_arith": "fp32", "protocol": "warm (back-to-back)" if args.warm else
@@ -400,6 +489,8 @@ def main():
     if dense is not None:
         dense["sparse_speedup"] = dense["ms_per_step"] / (total_ms / K)
         res["dense_baseline"] = dense
+    if sweep is not None:
+        res["granularity_sweep"] = sweep
     if edges is not None:
         res["prefill_edges"] = edges
     print(json.dumps(res), flush=True)

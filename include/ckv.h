@@ -103,9 +103,11 @@ typedef struct ckv_dims {
  * at elements kvh*d .. kvh*d+d-1); its score is the max over all query heads of
  * q_h . (head kvh(h)'s centroid) * scale; one index list serves every KV head;
  * the new token's key row (its Hkv keys, in order) joins the nearest candidate in
- * squared L2 over the whole row, and every KV head's K/V row n is written.  The
- * layer graph's update stages M centroid rows in LDS: M*(Hkv*d+4)*4 + Hkv*d*8
- * bytes must fit in 64 KiB, else CKV_ERR_UNSUPPORTED.  ckv_prefill_edges does not
+ * squared L2 over the whole row, accumulated per KV head (each head's slice in
+ * fp64 in element order, then the slices in head order), and every KV head's K/V
+ * row n is written.  The layer graph's update stages M centroid rows in LDS:
+ * Hkv <= 32, Hkv*d <= 4096 and M*(Hkv*d+4)*4 + Hkv*d*8 bytes within 64 KiB, else
+ * CKV_ERR_UNSUPPORTED.  ckv_prefill_edges does not
  * take the layer graph.
  */
 

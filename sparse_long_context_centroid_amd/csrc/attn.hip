@@ -463,23 +463,29 @@ __device__ __forceinline__ void merge_graph(int g, int Hq, int Hkv, int gpk,
         for (int s = lane; s < max_splits; s += kWave) s_w[hh * max_splits + s] *= inv;
     }
     __syncthreads();
-    if (tid >= GH * D) return;
-    float a = 0.f;
-    for (int s0 = 0; s0 < max_splits; s0 += kBatch) {
-        if (s0 > 0) {
+    // GH*D output elements over the workgroup's threads (more than one per thread
+    // when GH*D exceeds the workgroup: 8 heads x 128); the first element's first
+    // batch was loaded above
+    for (int t = tid; t < GH * D; t += blockDim.x) {
+        const int ht = t / D, it = t % D;
+        const float *pt = pbase + (size_t)ht * max_splits * (D + 2) + 2 + it;
+        float a = 0.f;
+        for (int s0 = 0; s0 < max_splits; s0 += kBatch) {
+            if (s0 > 0 || t != tid) {
 #pragma unroll
-            for (int k = 0; k < kBatch; ++k)
-                x[k] = s0 + k < max_splits ? pa[(size_t)(s0 + k) * (D + 2)] : 0.f;
-        }
+                for (int k = 0; k < kBatch; ++k)
+                    x[k] = s0 + k < max_splits ? pt[(size_t)(s0 + k) * (D + 2)] : 0.f;
+            }
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            if (s0 + k < max_splits) {
-                const float wk = s_w[h * max_splits + s0 + k];
-                if (wk != 0.f) a += x[k] * wk;
+            for (int k = 0; k < kBatch; ++k) {
+                if (s0 + k < max_splits) {
+                    const float wk = s_w[ht * max_splits + s0 + k];
+                    if (wk != 0.f) a += x[k] * wk;
+                }
             }
         }
+        out[((size_t)b * Hq + h0 + ht) * D + it] = a;
     }
-    out[((size_t)b * Hq + h0 + h) * D + i] = a;
 }
 
 // One workgroup per graph; with seq_len_bump (fused decode step) the first graph

@@ -125,33 +125,40 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
 // granularity section): a community carries one centroid per KV head, and its
 // score is the max over every query head h of q_h . mu_{c, kv head of h}:
 //   s[b][c] = max over KV heads k of fp32( max_{h in group k} (q_h . mu_{b,k,c}) * scale ).
-// The centroid of (b, k) is set b*Hkv + k of the interleaved layout.  The same
-// lane-per-community stream as above, once per KV head, with that head's G
-// queries restaged in LDS.
+// The centroid of (b, k) is set b*Hkv + k of the interleaved layout.  A workgroup
+// holds one wave per KV head (up to kLayerScoreWaves; more heads loop): each wave
+// runs the lane-per-community stream above on its head's slice with its G queries
+// in its own LDS rows, and the waves' maxima meet in LDS.
+constexpr int kLayerScoreWaves = 8;
+
 template <typename T, int D, int GH>
-__global__ __launch_bounds__(kScoreThreads) void layer_score_kernel(
+__global__ __launch_bounds__(kLayerScoreWaves * kWave) void layer_score_kernel(
     const T *__restrict__ q, const float *__restrict__ cent, const int32_t *__restrict__ num_comms,
     const int32_t *__restrict__ comm_size, int Cmax, int Hq, int Hkv, double scale,
     float *__restrict__ scores) {
     constexpr int KC = kScoreChunk;
     static_assert((D / 4) % KC == 0, "whole chunks");
-    constexpr int NQ = (D * GH / 4 + kScoreThreads - 1) / kScoreThreads;
-    __shared__ double sq[NQ * kScoreThreads * 4];
+    constexpr int NQ = (D * GH / 4 + kWave - 1) / kWave;
+    __shared__ double sq[kLayerScoreWaves][NQ * kWave * 4];
+    __shared__ float s_best[kLayerScoreWaves][kWave];
     const int b = blockIdx.y;
-    const int c0 = blockIdx.x * kScoreThreads + threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    const int c0 = blockIdx.x * kWave + lane;
     const int c = min(c0, Cmax - 1);
-    const int sz = comm_size[(size_t)b * Cmax + c];
     const int C = min(num_comms[b], Cmax);
-    if ((int)(blockIdx.x * kScoreThreads) >= C) return;
+    if ((int)(blockIdx.x * kWave) >= C) return;
     using Q4 = typename std::conditional<sizeof(T) == 2, uint2, float4>::type;
+    double *sqw = sq[w];
     float best = -__builtin_inff();
 #pragma unroll 1
-    for (int kvh = 0; kvh < Hkv; ++kvh) {
+    for (int kvh = w; kvh < Hkv; kvh += nw) {
         const int h0 = kvh * GH;
         Q4 qraw[NQ];
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
-            const int jq = min((int)threadIdx.x + j * kScoreThreads, D * GH / 4 - 1);
+            const int jq = min(lane + j * kWave, D * GH / 4 - 1);
             qraw[j] = *reinterpret_cast<const Q4 *>(q + ((size_t)b * Hq + h0 + jq % GH) * D +
                                                     (jq / GH) * 4);
         }
@@ -160,28 +167,28 @@ __global__ __launch_bounds__(kScoreThreads) void layer_score_kernel(
         float4 cur[KC];
 #pragma unroll
         for (int k = 0; k < KC; ++k) cur[k] = cp[(size_t)k * Cmax];
-        __syncthreads();  // the previous KV head's queries are no longer read
+        // this wave's previous head is no longer read (LDS rows private to the wave)
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             float e4[4];
             if constexpr (sizeof(T) == 2) {
-                const uint2 w = reinterpret_cast<const uint2 &>(qraw[j]);
-                e4[0] = bf16_lo(w.x);
-                e4[1] = bf16_hi(w.x);
-                e4[2] = bf16_lo(w.y);
-                e4[3] = bf16_hi(w.y);
+                const uint2 wv = reinterpret_cast<const uint2 &>(qraw[j]);
+                e4[0] = bf16_lo(wv.x);
+                e4[1] = bf16_hi(wv.x);
+                e4[2] = bf16_lo(wv.y);
+                e4[3] = bf16_hi(wv.y);
             } else {
-                const float4 w = reinterpret_cast<const float4 &>(qraw[j]);
-                e4[0] = w.x;
-                e4[1] = w.y;
-                e4[2] = w.z;
-                e4[3] = w.w;
+                const float4 wv = reinterpret_cast<const float4 &>(qraw[j]);
+                e4[0] = wv.x;
+                e4[1] = wv.y;
+                e4[2] = wv.z;
+                e4[3] = wv.w;
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                sq[(threadIdx.x + j * kScoreThreads) * 4 + e] = (double)e4[e];
+            for (int e = 0; e < 4; ++e) sqw[(lane + j * kWave) * 4 + e] = (double)e4[e];
         }
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
         double acc[GH];
 #pragma unroll
         for (int h = 0; h < GH; ++h) acc[h] = 0.0;
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(kScoreThreads) void layer_score_kernel(
                 const double e0 = cur[kk].x, e1 = cur[kk].y, e2 = cur[kk].z, e3 = cur[kk].w;
 #pragma unroll
                 for (int h = 0; h < GH; ++h) {
-                    const double *qq = sq + (k * GH + h) * 4;
+                    const double *qq = sqw + (k * GH + h) * 4;
                     acc[h] = fma(qq[0], e0, acc[h]);
                     acc[h] = fma(qq[1], e1, acc[h]);
                     acc[h] = fma(qq[2], e2, acc[h]);
@@ -214,7 +221,14 @@ __global__ __launch_bounds__(kScoreThreads) void layer_score_kernel(
         const float v = (float)(m * scale);
         best = v > best ? v : best;
     }
-    if (c0 < C) scores[(size_t)b * Cmax + c] = sz > 0 ? best : -__builtin_inff();
+    s_best[w][lane] = best;
+    __syncthreads();
+    if (w == 0) {
+        for (int i = 1; i < nw; ++i) best = s_best[i][lane] > best ? s_best[i][lane] : best;
+        if (c0 < C)
+            scores[(size_t)b * Cmax + c] =
+                comm_size[(size_t)b * Cmax + c] > 0 ? best : -__builtin_inff();
+    }
 }
 
 // ---- layout helpers ---------------------------------------------------------------
@@ -256,9 +270,10 @@ static void launch_score_t(const Problem &p, const void *q, const ckv_graphs &gr
 template <typename T, int D, int GH>
 static void launch_layer_score_t(const Problem &p, const void *q, const ckv_graphs &gr,
                                  double scale, float *scores, hipStream_t st) {
+    const int nw = p.Hkv < kLayerScoreWaves ? p.Hkv : kLayerScoreWaves;
     hipExtLaunchKernelGGL((layer_score_kernel<T, D, GH>),
-                          dim3((p.Cmax + kScoreThreads - 1) / kScoreThreads, p.B),
-                          dim3(kScoreThreads), 0, st, p.ev_start, p.ev_stop, 0,
+                          dim3((p.Cmax + kWave - 1) / kWave, p.B), dim3(nw * kWave), 0, st,
+                          p.ev_start, p.ev_stop, 0,
                           static_cast<const T *>(q), gr.centroids, gr.num_comms, gr.comm_size,
                           p.Cmax, p.Hq, p.Hkv, scale, scores);
 }

@@ -46,15 +46,18 @@ static void launch_update_t(const Problem &p, const void *k_new, const void *v_n
 // The layer graph: one graph per sequence b, whose centroid rows hold one d-slice
 // per KV head (E = Hkv*d values, KV head after KV head).  The new token's key row
 // is the concatenation of its Hkv keys; it joins the candidate whose row is
-// nearest in squared L2 over all E values (summed in fp64 in element order by the
-// candidate's lane; lower id on equal distance), that community's whole row moves
-// to the running mean, and K/V row n is written in every KV head.
+// nearest in squared L2 over all E values, accumulated per KV head (each slice
+// summed in fp64 in element order, then the slices in head order; lower id on
+// equal distance); that community's whole row moves to the running mean, and K/V
+// row n is written in every KV head.
 //
 // One workgroup per sequence: k_new is widened to fp64 in LDS and the candidates'
 // rows are staged there by the whole workgroup (every load in flight at once);
-// the first wave's lanes 0..M-1 then sum one distance each.  LDS: E doubles plus
-// M rows of E+4 floats (the host checks the size).
+// one thread per (candidate, slice) sums that slice, and the first wave's lanes
+// 0..M-1 add their candidate's slices in order.  LDS: E doubles plus M rows of
+// E+4 floats (the host checks the size).
 constexpr int kLayerUpdThreads = 256;
+constexpr int kLayerUpdMaxHeads = 32;  // KV heads (slices) per row
 inline size_t layer_update_lds(int E, int M) {
     return (size_t)E * sizeof(double) + (size_t)M * (E + 4) * sizeof(float);
 }
@@ -71,6 +74,8 @@ __global__ __launch_bounds__(kLayerUpdThreads) void layer_update_kernel(
 #pragma clang fp contract(off)
     extern __shared__ __align__(16) unsigned char s_raw[];
     __shared__ int s_best, s_slot, s_new;
+    __shared__ int s_cl[CKV_MAX_CAND];
+    __shared__ double s_part[CKV_MAX_CAND * kLayerUpdMaxHeads];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int E = Hkv * D, E4 = E / 4, CS = E + 4;
@@ -80,29 +85,74 @@ __global__ __launch_bounds__(kLayerUpdThreads) void layer_update_kernel(
     const int C = min(num_comms[b], Cmax);
     const T *kn = k_new + (size_t)b * E;
     const T *vn = v_new + (size_t)b * E;
-    for (int i = tid; i < E; i += kLayerUpdThreads) kn64[i] = (double)to_f32(kn[i]);
-    // candidate rows: element 4*k4 .. +3 of community c at float4 (b*E4 + k4)*Cmax + c
+    // round 1: the candidate ids (to LDS) and k_new (widened to fp64)
+    if (tid < M) {
+        const int cc = cand[(size_t)b * M + tid];
+        s_cl[tid] = (cc >= 0 && cc < C) ? cc : -1;
+    }
+    {
+        // E / 256 elements per thread, loaded together (clamped indexes: a loop of
+        // load-then-store would wait for each load in turn)
+        constexpr int kMaxPer = 16;  // E <= 4096
+        T kv[kMaxPer];
+#pragma unroll
+        for (int r = 0; r < kMaxPer; ++r) kv[r] = kn[min(tid + r * kLayerUpdThreads, E - 1)];
+#pragma unroll
+        for (int r = 0; r < kMaxPer; ++r)
+            if (tid + r * kLayerUpdThreads < E)
+                kn64[tid + r * kLayerUpdThreads] = (double)to_f32(kv[r]);
+    }
+    __syncthreads();
+    // round 2: the candidates' rows, element 4*k4 .. +3 of community c at float4
+    // (b*E4 + k4)*Cmax + c, 8 loads per thread in flight per pass
     const float4 *c4 = reinterpret_cast<const float4 *>(cent) + (size_t)b * E4 * Cmax;
-    for (int t = tid; t < M * E4; t += kLayerUpdThreads) {
-        const int sl = t / E4, k4 = t % E4;
-        const int cc = cand[(size_t)b * M + sl];
-        const int cl = (cc >= 0 && cc < C) ? cc : 0;
-        *reinterpret_cast<float4 *>(lc + sl * CS + 4 * k4) = c4[(size_t)k4 * Cmax + cl];
+    const int total = M * E4;
+    for (int t0 = 0; t0 < total; t0 += 8 * kLayerUpdThreads) {
+        float4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int t = min(t0 + k * kLayerUpdThreads + tid, total - 1);
+            v[k] = c4[(size_t)(t % E4) * Cmax + max(s_cl[t / E4], 0)];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // stores at the same clamped slots (past the end: a repeat of the last
+        // slot's own value), so no store waits behind a branch
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int t = min(t0 + k * kLayerUpdThreads + tid, total - 1);
+            *reinterpret_cast<float4 *>(lc + (t / E4) * CS + 4 * (t % E4)) = v[k];
+        }
+    }
+    __syncthreads();
+    // one (candidate, KV head slice) per thread: the slice's squared distance in
+    // element order, 4 at a time from LDS
+    for (int pr = tid; pr < M * Hkv; pr += kLayerUpdThreads) {
+        const int sl = pr / Hkv, kh = pr % Hkv;
+        const float4 *mu4 = reinterpret_cast<const float4 *>(lc + sl * CS + kh * D);
+        const double2 *k2 = reinterpret_cast<const double2 *>(kn64 + kh * D);
+        double s = 0.0;
+#pragma unroll 8
+        for (int i4 = 0; i4 < D / 4; ++i4) {
+            const float4 m = mu4[i4];
+            const double2 ka = k2[2 * i4], kb = k2[2 * i4 + 1];
+            const double d0 = ka.x - (double)m.x, d1 = ka.y - (double)m.y;
+            const double d2 = kb.x - (double)m.z, d3 = kb.y - (double)m.w;
+            const double q0 = d0 * d0, q1 = d1 * d1, q2 = d2 * d2, q3 = d3 * d3;
+            s = s + q0;
+            s = s + q1;
+            s = s + q2;
+            s = s + q3;
+        }
+        s_part[pr] = s;
     }
     __syncthreads();
     if (tid < kWave) {
         const int lane = tid;
-        const int cc = lane < M ? cand[(size_t)b * M + lane] : -1;
-        const int c = (cc >= 0 && cc < C) ? cc : -1;
+        const int c = lane < M ? s_cl[lane] : -1;
         double dist = __builtin_inf();
         if (c >= 0) {
             double s = 0.0;
-            const float *mu = lc + lane * CS;
-            for (int i = 0; i < E; ++i) {
-                const double diff = kn64[i] - (double)mu[i];
-                const double sq = diff * diff;
-                s = s + sq;
-            }
+            for (int kh = 0; kh < Hkv; ++kh) s = s + s_part[lane * Hkv + kh];
             dist = s;
         }
         int best = c, slot = c >= 0 ? lane : -1;
@@ -184,7 +234,8 @@ static void launch_layer_update_t(const Problem &p, const void *k_new, const voi
 }
 
 bool layer_update_fits(const Problem &p, int n_cand) {
-    return layer_update_lds(p.cdim(), n_cand) <= 65536;
+    return p.cdim() <= 4096 && p.Hkv <= kLayerUpdMaxHeads &&
+           layer_update_lds(p.cdim(), n_cand) <= 65536;
 }
 
 hipError_t launch_layer_update(const Problem &p, const void *k_new, const void *v_new,

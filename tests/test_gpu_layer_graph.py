@@ -58,6 +58,8 @@ _LAYER_SHAPES = [
                  layer_graph=True),
     I.ConfigSpec("bf16-d128-g1-layer", 2, 4, 4, 128, 2000, False, 200, 3, I.DT_BF16,
                  layer_graph=True),
+    I.ConfigSpec("bf16-d128-g8-layer", 1, 16, 2, 128, 2300, False, 256, 2, I.DT_BF16,
+                 layer_graph=True),
 ]
 
 

@@ -164,6 +164,8 @@ def test_parity_full_size_ragged_paged_deep_layer():
     (1, dict(context=6000, steps=1), None),
     (4, dict(contexts=[8192, 3000, 12345, 700], steps=1, layers=1), None),
     (3, dict(steps=1), 12),
+    (I.ConfigSpec("bf16-d128-g8-group", 2, 16, 2, 128, 2300, False, 256, 1, I.DT_BF16),
+     dict(), None),
 ])
 def test_dense_baseline_matches_oracle(cfg, kw, sample):
     """The dense baseline (every cached token, through the page table) against the
@@ -236,6 +238,8 @@ _SHAPES = [
     I.ConfigSpec("fp32-d64-g1-mha", 1, 2, 2, 64, 1500, False, 128, 2, I.DT_F32),
     I.ConfigSpec("bf16-d128-g2-group", 3, 8, 4, 128, 1800, False, 160, 2, I.DT_BF16),
     I.ConfigSpec("fp32-d64-g8-group", 1, 8, 1, 64, 2600, False, 256, 2, I.DT_F32),
+    # 8 heads x d 128 = 1024 outputs per graph: more than the merge's 512 threads
+    I.ConfigSpec("bf16-d128-g8-group", 2, 16, 2, 128, 2300, False, 256, 2, I.DT_BF16),
 ]
 
 
