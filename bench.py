@@ -14,8 +14,14 @@ centroids, lists or KV rows; the step itself is bracketed by HIP events on the
 stream the kernels run on (launch gaps included), and each kernel carries its own
 start / stop events bound to its execution.  `value` = tokens (decode tokens of
 all sequences) / sum of the bracketed step times; the roofline uses the bound
-kernel duration.  `--warm` drops the scrub (back-to-back steps).  Inputs are
-resident in HBM before timing starts.
+kernel duration.  `--warm` drops the scrub (back-to-back steps); without it a
+short back-to-back pass follows the cold passes and is reported as `warm`.
+Inputs are resident in HBM before timing starts.
+
+Besides the step, one run also reports: the dense baseline on the same cache,
+the centroid rebuild and drift, the graph-granularity sweep (group, per query
+head, per layer: step time and graph memory), the prefill edge kernel against
+the bf16 MFMA peak, and the fp64 oracle on the host cores (all threads and one).
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
@@ -297,6 +303,16 @@ def build_layers(wl, index_stride):
     return layers
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, seconds: float, threads: int):
     """The fp64 oracle on the host cores, on the first steps of layer 0."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -356,7 +372,9 @@ def main():
     torch.cuda.set_device(0)
     # warmup, then K steps timed as a whole (value), then K steps with per-kernel
     # events (roofline); the per-kernel events are kept out of the value pass
-    T = args.warmup + 2 * args.steps
+    # ... then (cold protocol only) a few back-to-back steps without the scrub
+    KW = 0 if args.warm else min(args.steps, 20)
+    T = args.warmup + 2 * args.steps + KW
     spec = I.CONFIGS[args.config]
     if args.graphs != "config":
         spec = I.granularity_spec(spec, args.graphs)
@@ -372,7 +390,12 @@ def main():
         threads = min(len(os.sched_getaffinity(0)), 16)
         t1 = time.perf_counter()
         cpu = cpu_baseline(wl, args.cpu_seconds, threads)
-        log(f"[bench] cpu baseline {cpu['value']:.1f} tokens/s ({time.perf_counter() - t1:.1f}s)")
+        one = cpu_baseline(wl, max(2.0, args.cpu_seconds / 5), 1)
+        cpu["value_1_thread"] = one["value"]
+        cpu["sample_1_thread"] = one["sample"]
+        cpu["cpu_model"] = cpu_model()
+        log(f"[bench] cpu baseline {cpu['value']:.1f} tokens/s, 1 thread {one['value']:.1f} "
+            f"({time.perf_counter() - t1:.1f}s)")
     layers = build_layers(wl, index_stride)
     timers = [Timed(l) for l in layers]
     elem = 2 if wl.dtype == I.DT_BF16 else 4
@@ -388,19 +411,22 @@ def main():
     kernel_ms = np.zeros(4)
     kernel_bytes = {k: 0 for k in KERNELS}
     attn_only_bytes = 0
-    step_ms, step_ms_instr = [], []
+    step_ms, step_ms_instr, step_ms_warm = [], [], []
     value_bytes = 0
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for t in range(T):
-        phase = 0 if t < args.warmup else (1 if t < args.warmup + args.steps else 2)
+        phase = 0 if t < args.warmup else (1 if t < args.warmup + args.steps else (
+            2 if t < args.warmup + 2 * args.steps else 3))
         tot = 0.0
         for li, (tm, (q, kn, vn)) in enumerate(zip(timers, qkv)):
-            if not args.warm:
+            if not args.warm and phase != 3:
                 scrub_sum = scrub.sum()               # cold caches, outside the events
             tm.run(q[t], kn[t], vn[t], wl.scale, per_kernel=phase == 2)
             torch.cuda.synchronize()
-            if phase:
+            if phase == 3:
+                tot += tm.step_ms()
+            elif phase:
                 tot += tm.step_ms()
                 idx_len = tm.layer.index_len.cpu().numpy()
                 by, ab = step_bytes(tm.layer, idx_len, elem)
@@ -415,6 +441,8 @@ def main():
             step_ms.append(tot)
         elif phase == 2:
             step_ms_instr.append(tot)
+        elif phase == 3:
+            step_ms_warm.append(tot)
         if t == 0 or (t + 1) % 10 == 0:
             log(f"[bench] step {t + 1}/{T}")
     wall = time.perf_counter() - wall0
@@ -452,6 +480,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": total_ms / K,
+        "ms_per_step_median": float(np.median(step_ms)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -471,6 +500,10 @@ def main():
         "path_frac_hbm": all_bytes / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         "bytes_per_step": all_bytes / K,
         "ms_per_step_with_kernel_events": float(np.mean(step_ms_instr)),
+        "warm": ({"ms_per_step": float(np.mean(step_ms_warm)),
+                  "tokens_per_s": wl.B / (float(np.mean(step_ms_warm)) / 1e3),
+                  "steps": len(step_ms_warm),
+                  "protocol": "back-to-back steps, no scrub"} if step_ms_warm else None),
         "kernels": per_kernel,
         "attn_share_of_attn_update_bytes": attn_only_bytes / kernel_bytes["attn_update"],
         "wall_s_timed_loop": wall,
