@@ -33,7 +33,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kEdgeWaves = 4;
+#ifndef CKV_EDGE_WAVES
+#define CKV_EDGE_WAVES 4
+#endif
+constexpr int kEdgeWaves = CKV_EDGE_WAVES;  // waves (query blocks) sharing a key tile
 #ifndef CKV_EDGE_KT
 #define CKV_EDGE_KT 64
 #endif
@@ -43,7 +46,14 @@ constexpr int kEdgeList = 8; // list length kept per query (largest topk)
 #define CKV_EDGE_REFRESH 4
 #endif
 constexpr int kEdgeRefresh = CKV_EDGE_REFRESH;  // tiles between row-bound refreshes
-constexpr int edge_queries_per_wave(int hpg) { return hpg <= 4 ? 16 : 8; }
+#ifndef CKV_EDGE_QPW1
+#define CKV_EDGE_QPW1 16
+#endif
+// queries per wave: 64 MFMA rows of (query, head) pairs, or with one head per
+// graph CKV_EDGE_QPW1 queries (16 or 32: two M-blocks share each key block)
+constexpr int edge_queries_per_wave(int hpg) {
+    return hpg == 1 ? CKV_EDGE_QPW1 : (hpg <= 4 ? 16 : 8);
+}
 
 // (a, ia) before (b, ib) in the (score desc, position asc) order.
 __device__ __forceinline__ bool edge_before(float a, int ia, float b, int ib) {
@@ -104,7 +114,7 @@ __global__ __launch_bounds__(kEdgeWaves * kWave) void edges_kernel(
     constexpr int KT = kEdgeKT;
     constexpr int kPieces = KT * D / 8 / (kEdgeWaves * kWave);  // 16-byte loads per thread
     static_assert(HPG == 1 || HPG == 2 || HPG == 4 || HPG == 8, "heads per graph");
-    static_assert(NQ == 4, "query slots");
+    static_assert(NQ == 4 || NQ == 8, "query slots");
     static_assert(kPieces * kEdgeWaves * kWave * 8 == KT * D, "tile split");
     __shared__ __align__(16) bf16_t s_k[2][KT * LDSR];
 
