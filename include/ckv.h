@@ -39,7 +39,9 @@
  *   KV head kvh and sub-index j is g = (b*num_kv_heads + kvh)*graphs_per_kv + j.
  *   With graphs_per_kv == 1 the G = num_q_heads/num_kv_heads query heads
  *   kvh*G .. kvh*G+G-1 share one graph (query-group graph); with
- *   graphs_per_kv == G query head kvh*G + j owns graph g (per-head graph).
+ *   graphs_per_kv == G query head kvh*G + j owns graph g (per-head graph); with
+ *   graphs_per_kv == 0 graph g = b serves every head of the layer (NG = batch;
+ *   see "Graph granularity" below).
  * - Not reentrant across overlapping calls that share a workspace.
  */
 #ifndef CKV_H
@@ -311,6 +313,8 @@ CKV_API ckv_status ckv_prefill_edges(const ckv_dims *dims, const void *q, const 
  * start / stop pair of each of the 4 kernels in the order above, bound to the
  * kernel's own execution (hipExtLaunchKernelGGL), so hipEventElapsedTime of a
  * pair is that kernel's duration without launch gaps.
+ * The layer graph (graphs_per_kv = 0) takes 5 launches: its update runs as its
+ * own launch between the attention and the merge (not covered by the events).
  */
 CKV_API ckv_status ckv_decode_step(const ckv_dims *dims, const void *q, const void *k_new,
                                    const void *v_new, const ckv_graphs *graphs, const ckv_kv *kv,
