@@ -31,6 +31,8 @@
 //   partials: m* = max m_s, l = sum l_s 2^(m_s-m*), o = sum acc_s 2^(m_s-m*) / l.
 // * In the fused decode step grid row 0 holds extra workgroups, one wave per
 //   graph, that run the local update while the other workgroups stream K/V.
+#include <type_traits>
+
 #include "ckv_device.h"
 #include "ckv_internal.h"
 #include "update_rule.h"
@@ -299,44 +301,58 @@ __global__ __launch_bounds__(256) void attn_kernel(
     // the gather into dependent round trips
     __builtin_amdgcn_sched_barrier(0);
 
-    // online softmax over batches of kSub loads; m, l, acc are per row slot
+    // online softmax over batches of kSub loads; m, l, acc are per row slot.  m is
+    // a reference, not necessarily the running maximum: (l, acc) are rescaled only
+    // when a logit exceeds it by more than 2^kLazy (so p = 2^(z-m) <= 2^kLazy and
+    // acc stays far from fp32 overflow); (m, l, acc) always describe the same sum.
+    // MASKED: rows past the chunk's end take no part (z = -inf, p = 0).
+    auto fold = [&](auto masked_c) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_c)::value;
+        constexpr float kLazy = 8.f;
 #pragma unroll
-    for (int i0 = 0; i0 < NLD; i0 += kSub) {
-        float z[kSub][GH];
+        for (int i0 = 0; i0 < NLD; i0 += kSub) {
+            float z[kSub][GH];
 #pragma unroll
-        for (int j = 0; j < kSub; ++j) {
+            for (int j = 0; j < kSub; ++j) {
+#pragma unroll
+                for (int h = 0; h < GH; ++h) {
+                    const float s = group_sum<LPR>(qk_part<T, EPL>(qp[h], qf[h], kr[i0 + j]));
+                    z[j][h] = s * scale_log2;
+                    if constexpr (MASKED)
+                        z[j][h] = (valid >> (i0 + j)) & 1u ? z[j][h] : -__builtin_inff();
+                }
+            }
 #pragma unroll
             for (int h = 0; h < GH; ++h) {
-                const float s = group_sum<LPR>(qk_part<T, EPL>(qp[h], qf[h], kr[i0 + j]));
-                z[j][h] = (valid >> (i0 + j)) & 1u ? s * scale_log2 : -__builtin_inff();
+                float mn = m[h];
+#pragma unroll
+                for (int j = 0; j < kSub; ++j) mn = fmaxf(mn, z[j][h]);
+                if (mn > m[h] + kLazy) {
+                    const float c = fast_exp2(m[h] - mn);  // 0 when m was -inf
+                    l[h] *= c;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[h][e] *= c;
+                    m[h] = mn;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kSub; ++j) {
+                float x[EPL];
+                unpack<T, EPL>(vr[i0 + j], x);
+#pragma unroll
+                for (int h = 0; h < GH; ++h) {
+                    float p = fast_exp2(z[j][h] - m[h]);
+                    if constexpr (MASKED) p = (valid >> (i0 + j)) & 1u ? p : 0.f;
+                    l[h] += p;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
+                }
             }
         }
-#pragma unroll
-        for (int h = 0; h < GH; ++h) {
-            float mn = m[h];
-#pragma unroll
-            for (int j = 0; j < kSub; ++j) mn = fmaxf(mn, z[j][h]);
-            if (mn != -__builtin_inff()) {
-                const float c = fast_exp2(m[h] - mn);  // 0 when m was -inf
-                l[h] *= c;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[h][e] *= c;
-                m[h] = mn;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kSub; ++j) {
-            float x[EPL];
-            unpack<T, EPL>(vr[i0 + j], x);
-#pragma unroll
-            for (int h = 0; h < GH; ++h) {
-                const float p = (valid >> (i0 + j)) & 1u ? fast_exp2(z[j][h] - m[h]) : 0.f;
-                l[h] += p;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
-            }
-        }
-    }
+    };
+    // (one masked body: a second, unmasked copy for full chunks measured slower --
+    // the doubled unrolled body costs more than the selects it saves)
+    fold(std::integral_constant<bool, true>{});
     };
     if constexpr (MODE == kAttnDense) {
         for (int c0 = t_begin; c0 < t_end; c0 += CH) {
