@@ -69,6 +69,16 @@ __device__ __forceinline__ int graph_of_column(int x, int NG, int gpk) {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Maximum over the 16 lanes of a row, in every lane of the row.
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    return fmaxf(x, dpp<0x140>(x));
+}
 
 struct OpAdd {
     __device__ float operator()(float a, float b) const { return a + b; }
@@ -174,6 +184,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
     __shared__ float s_m[kAttnWaves][GH];
     __shared__ float s_l[kAttnWaves][GH];
     __shared__ float s_acc[kAttnWaves][GH][D];
+    __shared__ __align__(16) float s_p[kAttnWaves][16 * GH];  // bf16 path: p of one group
 
     if constexpr (MODE == kAttnIndexedUpdate) {
         // grid row 0: the local update, one wave per graph (dispatched first, so it
@@ -225,23 +236,47 @@ __global__ __launch_bounds__(256) void attn_kernel(
     const int ls = lane % LPR;  // slice of the row this lane reads
     const int rs = lane / LPR;  // row slot inside a wave-wide load
 
+    // bf16 rows: q.K of 16 rows at a time on the matrix cores; fp32 rows: dot
+    // products on the vector ALUs (below)
+    constexpr bool kMfma = sizeof(T) == 2;
+    const int r16 = lane & 15, t4 = lane >> 4;  // matrix-core lane coordinates
+
     // query slice: packed bf16 pairs (dot2) or fp32; the scale is applied to the sum
     uint32_t qp[GH][NQP];
     float qf[GH][EPL];
+    // matrix-core A operand (bf16): row r16 is head r16 % GH (the heads repeat down
+    // the 16 rows), k-block j of 32 elements, this lane's 8 at 32j + 8*t4
+    constexpr int KB = kMfma ? D / 32 : 1;
+    bf16x8_t qa[KB];
+    if constexpr (kMfma) {
 #pragma unroll
-    for (int h = 0; h < GH; ++h) {
-        const uint4 u =
-            *reinterpret_cast<const uint4 *>(q + ((size_t)b * Hq + h0 + h) * D + ls * EPL);
-        if constexpr (sizeof(T) == 2) {
-            qp[h][0] = u.x; qp[h][1] = u.y; qp[h][2] = u.z; qp[h][3] = u.w;
-        } else {
+        for (int j = 0; j < KB; ++j)
+            qa[j] = *reinterpret_cast<const bf16x8_t *>(
+                q + ((size_t)b * Hq + h0 + r16 % GH) * D + 32 * j + 8 * t4);
+    } else {
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
+            const uint4 u =
+                *reinterpret_cast<const uint4 *>(q + ((size_t)b * Hq + h0 + h) * D + ls * EPL);
             qf[h][0] = __uint_as_float(u.x); qf[h][1] = __uint_as_float(u.y);
             qf[h][2] = __uint_as_float(u.z); qf[h][3] = __uint_as_float(u.w);
         }
     }
 
-    // running (m, l, acc) of this lane's row slot, over all chunks of the piece
+    // fp32 path: running (m, l, acc) of this lane's row slot
     float m[GH], l[GH], acc[GH][EPL];
+    // bf16 path: one reference per head for the whole wave (mv, in the scaled log2
+    // domain), and lane partial sums of p; register i of a lane serves head
+    // (4*t4 + i) % GH, the head of accumulator row 4*t4 + i
+    float mv[4], thr[4], lsum[4];
+    constexpr float kLazy = 8.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // finite start: z > thr holds for every finite logit, and 2^(-inf - mv) = 0
+        mv[i] = -__FLT_MAX__;
+        thr[i] = -__FLT_MAX__;
+        lsum[i] = 0.f;
+    }
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
         m[h] = -__builtin_inff();
@@ -250,7 +285,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
         for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
     }
     // one chunk of at most CH tokens [c0, c_end): rows to LDS, then the K/V rows of
-    // this lane's slots, folded into (m, l, acc)
+    // this wave, folded into the running state
     auto chunk = [&](const int c0, const int c_end) {
     // ---- phase A: list entries -> row indices in LDS
     for (int t = tid; t < CH; t += blockDim.x) {
@@ -273,7 +308,131 @@ __global__ __launch_bounds__(256) void attn_kernel(
     }
     __syncthreads();
 
-    // ---- phase B: this lane's NLD row slots are contiguous in LDS
+    if constexpr (kMfma) {
+        // ---- phase B (bf16).  The wave's TPW tokens form NGRP groups of 16 rows.
+        // K: MFMA B operand, lane (r16, t4) holds row r16 of the group, elements
+        // 32j + 8*t4 .. +7 for k-block j (one wave-wide load per k-block: 64 B of
+        // each of the 16 rows).  V: the plain layout, LPR lanes per row, RPW rows per
+        // load; lane slot rs takes rows rs*VL .. rs*VL + VL-1 of the group.
+        constexpr int NGRP = TPW / 16;
+        constexpr int VL = 16 / RPW;
+        static_assert(TPW % 16 == 0 && VL == KB && NGRP * VL == NLD, "group shape");
+        const int *sw = s_row + w * TPW;
+        int krow[NGRP], vrow[NGRP][VL];
+#pragma unroll
+        for (int gi = 0; gi < NGRP; ++gi) {
+            krow[gi] = sw[16 * gi + r16];
+            if constexpr (VL == 4) {
+                const int4 r4 = *reinterpret_cast<const int4 *>(sw + 16 * gi + rs * VL);
+                vrow[gi][0] = r4.x; vrow[gi][1] = r4.y; vrow[gi][2] = r4.z; vrow[gi][3] = r4.w;
+            } else {
+                static_assert(VL == 2, "V loads per group");
+                const int2 r2 = *reinterpret_cast<const int2 *>(sw + 16 * gi + rs * VL);
+                vrow[gi][0] = r2.x; vrow[gi][1] = r2.y;
+            }
+        }
+        uint32_t kvalid = 0;
+#pragma unroll
+        for (int gi = 0; gi < NGRP; ++gi) kvalid |= (krow[gi] >= 0 ? 1u : 0u) << gi;
+        // all loads in flight together, K then V of each group in turn, so the
+        // first group can start while the later ones arrive
+        uint4 kb[NGRP][KB], vr[NGRP][VL];
+#pragma unroll
+        for (int gi = 0; gi < NGRP; ++gi) {
+            const size_t kr = (size_t)(krow[gi] < 0 ? 0 : krow[gi]) * D;
+#pragma unroll
+            for (int j = 0; j < KB; ++j) kb[gi][j] = load_nt(kc + kr + 32 * j + 8 * t4);
+#pragma unroll
+            for (int jj = 0; jj < VL; ++jj)
+                vr[gi][jj] = load_nt(vc + (size_t)(vrow[gi][jj] < 0 ? 0 : vrow[gi][jj]) * D +
+                                     ls * EPL);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        float *sp = s_p[w];
+#pragma unroll
+        for (int gi = 0; gi < NGRP; ++gi) {
+            // S[4*t4 + i][r16] = q_head . K_row over KB k-blocks
+            f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KB; ++j)
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    qa[j], __builtin_bit_cast(bf16x8_t, kb[gi][j]), c, 0, 0, 0);
+            const bool ok = (kvalid >> gi) & 1u;
+            float z[4];
+            bool need = false;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                z[i] = ok ? c[i] * scale_log2 : -__builtin_inff();
+                need |= z[i] > thr[i];
+            }
+            // lazy reference: (l, acc) are rescaled only when a logit of the wave
+            // passes its head's reference by more than 2^kLazy, so p <= 2^kLazy
+            if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                float cf[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float mn = fmaxf(mv[i], row_max16(z[i]));
+                    cf[i] = fast_exp2(mv[i] - mn);
+                    mv[i] = mn;
+                    thr[i] = mn + kLazy;
+                    lsum[i] *= cf[i];
+                }
+                float hf[GH];  // the factor of each head, in every lane
+                if constexpr (GH <= 4) {
+#pragma unroll
+                    for (int h = 0; h < GH; ++h) hf[h] = cf[h];
+                } else {
+                    // heads 0-3 sit in even 16-lane rows, 4-7 in odd ones
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t u = __float_as_uint(cf[i]);
+                        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+                        hf[i] = __uint_as_float(r[0]);
+                        hf[4 + i] = __uint_as_float(r[1]);
+                    }
+                }
+#pragma unroll
+                for (int h = 0; h < GH; ++h)
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[h][e] *= hf[h];
+            }
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = fast_exp2(z[i] - mv[i]);
+                lsum[i] += p[i];
+            }
+            // p of (row r16, head) to the wave's LDS slots, read back in the V layout
+            // (lanes repeating a head store the same value)
+            if constexpr (GH == 8)
+                *reinterpret_cast<float4 *>(sp + r16 * 8 + 4 * (t4 & 1)) =
+                    make_float4(p[0], p[1], p[2], p[3]);
+            else if constexpr (GH == 4)
+                *reinterpret_cast<float4 *>(sp + r16 * 4) = make_float4(p[0], p[1], p[2], p[3]);
+            else if constexpr (GH == 2)
+                *reinterpret_cast<float2 *>(sp + r16 * 2) = make_float2(p[0], p[1]);
+            else
+                sp[r16] = p[0];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+            for (int jj = 0; jj < VL; ++jj) {
+                const float *pr = sp + (rs * VL + jj) * GH;
+                float pv[GH];
+#pragma unroll
+                for (int h = 0; h < GH; ++h) pv[h] = pr[h];
+                float x[EPL];
+                unpack<T, EPL>(vr[gi][jj], x);
+#pragma unroll
+                for (int h = 0; h < GH; ++h)
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pv[h], x[e], acc[h][e]);
+            }
+            // the next group's stores must not overtake these loads
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    } else {
+    // ---- phase B (fp32): this lane's NLD row slots are contiguous in LDS
     int rows[NLD];
     {
         const int4 *sr = reinterpret_cast<const int4 *>(s_row + w * TPW + rs * NLD);
@@ -305,54 +464,46 @@ __global__ __launch_bounds__(256) void attn_kernel(
     // a reference, not necessarily the running maximum: (l, acc) are rescaled only
     // when a logit exceeds it by more than 2^kLazy (so p = 2^(z-m) <= 2^kLazy and
     // acc stays far from fp32 overflow); (m, l, acc) always describe the same sum.
-    // MASKED: rows past the chunk's end take no part (z = -inf, p = 0).
-    auto fold = [&](auto masked_c) __attribute__((always_inline)) {
-        constexpr bool MASKED = decltype(masked_c)::value;
-        constexpr float kLazy = 8.f;
+    // Rows past the chunk's end take no part (z = -inf, p = 0).
 #pragma unroll
-        for (int i0 = 0; i0 < NLD; i0 += kSub) {
-            float z[kSub][GH];
+    for (int i0 = 0; i0 < NLD; i0 += kSub) {
+        float z[kSub][GH];
 #pragma unroll
-            for (int j = 0; j < kSub; ++j) {
-#pragma unroll
-                for (int h = 0; h < GH; ++h) {
-                    const float s = group_sum<LPR>(qk_part<T, EPL>(qp[h], qf[h], kr[i0 + j]));
-                    z[j][h] = s * scale_log2;
-                    if constexpr (MASKED)
-                        z[j][h] = (valid >> (i0 + j)) & 1u ? z[j][h] : -__builtin_inff();
-                }
-            }
+        for (int j = 0; j < kSub; ++j) {
 #pragma unroll
             for (int h = 0; h < GH; ++h) {
-                float mn = m[h];
-#pragma unroll
-                for (int j = 0; j < kSub; ++j) mn = fmaxf(mn, z[j][h]);
-                if (mn > m[h] + kLazy) {
-                    const float c = fast_exp2(m[h] - mn);  // 0 when m was -inf
-                    l[h] *= c;
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) acc[h][e] *= c;
-                    m[h] = mn;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < kSub; ++j) {
-                float x[EPL];
-                unpack<T, EPL>(vr[i0 + j], x);
-#pragma unroll
-                for (int h = 0; h < GH; ++h) {
-                    float p = fast_exp2(z[j][h] - m[h]);
-                    if constexpr (MASKED) p = (valid >> (i0 + j)) & 1u ? p : 0.f;
-                    l[h] += p;
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
-                }
+                const float s = group_sum<LPR>(qk_part<T, EPL>(qp[h], qf[h], kr[i0 + j]));
+                z[j][h] = (valid >> (i0 + j)) & 1u ? s * scale_log2 : -__builtin_inff();
             }
         }
-    };
-    // (one masked body: a second, unmasked copy for full chunks measured slower --
-    // the doubled unrolled body costs more than the selects it saves)
-    fold(std::integral_constant<bool, true>{});
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
+            float mn = m[h];
+#pragma unroll
+            for (int j = 0; j < kSub; ++j) mn = fmaxf(mn, z[j][h]);
+            if (mn > m[h] + kLazy) {
+                const float c = fast_exp2(m[h] - mn);  // 0 when m was -inf
+                l[h] *= c;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[h][e] *= c;
+                m[h] = mn;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            float x[EPL];
+            unpack<T, EPL>(vr[i0 + j], x);
+#pragma unroll
+            for (int h = 0; h < GH; ++h) {
+                float p = fast_exp2(z[j][h] - m[h]);
+                p = (valid >> (i0 + j)) & 1u ? p : 0.f;
+                l[h] += p;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
+            }
+        }
+    }
+    }
     };
     if constexpr (MODE == kAttnDense) {
         for (int c0 = t_begin; c0 < t_end; c0 += CH) {
@@ -362,6 +513,36 @@ __global__ __launch_bounds__(256) void attn_kernel(
     } else {
         chunk(t_begin, t_end);  // an indexed piece is one chunk
     }
+    if constexpr (kMfma) {
+        // one reference per head: the RPW row slots of acc simply add up; l is the
+        // sum of p over the 16 rows of a 16-lane row
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                if constexpr (LPR <= 8) acc[h][e] = pair_op<8>(acc[h][e], OpAdd{});
+                if constexpr (LPR <= 16) acc[h][e] = pair_op<16>(acc[h][e], OpAdd{});
+                acc[h][e] = pair_op<32>(acc[h][e], OpAdd{});
+            }
+        }
+        float lt[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lt[i] = group_sum<16>(lsum[i]);
+        if (lane < LPR) {
+#pragma unroll
+            for (int h = 0; h < GH; ++h)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) s_acc[w][h][lane * EPL + e] = acc[h][e];
+        }
+        // lane 0 holds heads 0..min(GH,4)-1, lane 16 heads 4-7
+        if (r16 == 0 && t4 < (GH > 4 ? 2 : 1)) {
+#pragma unroll
+            for (int i = 0; i < (GH < 4 ? GH : 4); ++i) {
+                s_m[w][4 * t4 + i] = mv[i];
+                s_l[w][4 * t4 + i] = lt[i];
+            }
+        }
+    } else {
     // merge the RPW row slots of the wave (same dims, disjoint tokens, own maxima);
     // lanes L and L^off pair up with VALU lane swaps, no LDS round trips
 #pragma unroll
@@ -399,6 +580,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
                 s_l[w][h] = l[h];
             }
         }
+    }
     }
     __syncthreads();
 
