@@ -180,18 +180,24 @@ __global__ __launch_bounds__(256) void attn_kernel(
     static_assert(LPR >= 1 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "row split");
     static_assert(NLD % 4 == 0 && NLD % kSub == 0, "row slots are read as int4");
 
+    constexpr bool kMfma = sizeof(T) == 2;  // bf16: q.K on the matrix cores
     __shared__ __align__(16) int s_row[CH];
     __shared__ float s_m[kAttnWaves][GH];
     __shared__ float s_l[kAttnWaves][GH];
     __shared__ float s_acc[kAttnWaves][GH][D];
     __shared__ __align__(16) float s_p[kAttnWaves][16 * GH];  // bf16 path: p of one group
+    // bf16 path: per wave, the K rows of one 16-row group (16 x D bf16), shared with
+    // the fused update's rows (grid row 0 runs only the update)
+    // plus the graph's GH query rows (bf16) after the tiles
+    constexpr int kStageFloats = kMfma ? kAttnWaves * 16 * D / 2 + GH * D / 2 : 1;
+    constexpr int kUpdFloats = MODE == kAttnIndexedUpdate ? kAttnWaves * kUpdLdsFloats(D) : 1;
+    __shared__ __align__(16) float s_big[kStageFloats > kUpdFloats ? kStageFloats : kUpdFloats];
 
     if constexpr (MODE == kAttnIndexedUpdate) {
         // grid row 0: the local update, one wave per graph (dispatched first, so it
         // runs under the K/V stream of the attention workgroups); seq_len advances
         // in the merge launch
         if (blockIdx.y == 0) {
-            __shared__ __align__(16) float s_upd[kAttnWaves * kUpdLdsFloats(D)];
             const int w = threadIdx.x / kWave;
             const size_t gu = (size_t)blockIdx.x * kAttnWaves + w;
             if (gu < u.NG)
@@ -200,7 +206,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
                                    u.num_comms, u.comm_start, u.comm_size, u.comm_cap, u.members,
                                    u.Cmax, Hkv, gpk, kc, vc, page_table, log2ps, max_pages,
                                    num_pages, seq_len, u.assigned, err,
-                                   s_upd + w * kUpdLdsFloats(D));
+                                   s_big + w * kUpdLdsFloats(D));
             return;
         }
     }
@@ -238,21 +244,22 @@ __global__ __launch_bounds__(256) void attn_kernel(
 
     // bf16 rows: q.K of 16 rows at a time on the matrix cores; fp32 rows: dot
     // products on the vector ALUs (below)
-    constexpr bool kMfma = sizeof(T) == 2;
     const int r16 = lane & 15, t4 = lane >> 4;  // matrix-core lane coordinates
 
     // query slice: packed bf16 pairs (dot2) or fp32; the scale is applied to the sum
     uint32_t qp[GH][NQP];
     float qf[GH][EPL];
     // matrix-core A operand (bf16): row r16 is head r16 % GH (the heads repeat down
-    // the 16 rows), k-block j of 32 elements, this lane's 8 at 32j + 8*t4
+    // the 16 rows), k-block j of 32 elements, this lane's 8 at 32j + 8*t4.  The GH
+    // query rows wait in LDS behind the K tiles and are read per group, which keeps
+    // 16 registers free for loads in flight.
     constexpr int KB = kMfma ? D / 32 : 1;
-    bf16x8_t qa[KB];
+    const uint4 *s_q = reinterpret_cast<const uint4 *>(s_big + kAttnWaves * 16 * D / 2);
     if constexpr (kMfma) {
-#pragma unroll
-        for (int j = 0; j < KB; ++j)
-            qa[j] = *reinterpret_cast<const bf16x8_t *>(
-                q + ((size_t)b * Hq + h0 + r16 % GH) * D + 32 * j + 8 * t4);
+        for (int t = tid; t < GH * D / 8; t += blockDim.x)
+            reinterpret_cast<uint4 *>(s_big + kAttnWaves * 16 * D / 2)[t] =
+                reinterpret_cast<const uint4 *>(q + ((size_t)b * Hq + h0) * D)[t];
+        // (visible after phase A's barrier)
     } else {
 #pragma unroll
         for (int h = 0; h < GH; ++h) {
@@ -310,18 +317,19 @@ __global__ __launch_bounds__(256) void attn_kernel(
 
     if constexpr (kMfma) {
         // ---- phase B (bf16).  The wave's TPW tokens form NGRP groups of 16 rows.
-        // K: MFMA B operand, lane (r16, t4) holds row r16 of the group, elements
-        // 32j + 8*t4 .. +7 for k-block j (one wave-wide load per k-block: 64 B of
-        // each of the 16 rows).  V: the plain layout, LPR lanes per row, RPW rows per
-        // load; lane slot rs takes rows rs*VL .. rs*VL + VL-1 of the group.
+        // K and V rows are both read whole, LPR lanes per row and RPW rows per load;
+        // lane slot rs takes rows rs*VL .. rs*VL + VL-1 of a group.  Each group's K
+        // rows then pass through this wave's LDS tile into the MFMA B operand: lane
+        // (r16, t4) needs row r16, elements 32j + 8*t4 .. +7 for k-block j.  The
+        // 16-byte pieces of row r sit at slot (piece ^ swz(r)) in the tile, so both
+        // the row-wise writes and the column-wise reads spread over all banks.
         constexpr int NGRP = TPW / 16;
         constexpr int VL = 16 / RPW;
         static_assert(TPW % 16 == 0 && VL == KB && NGRP * VL == NLD, "group shape");
         const int *sw = s_row + w * TPW;
-        int krow[NGRP], vrow[NGRP][VL];
+        int vrow[NGRP][VL];
 #pragma unroll
         for (int gi = 0; gi < NGRP; ++gi) {
-            krow[gi] = sw[16 * gi + r16];
             if constexpr (VL == 4) {
                 const int4 r4 = *reinterpret_cast<const int4 *>(sw + 16 * gi + rs * VL);
                 vrow[gi][0] = r4.x; vrow[gi][1] = r4.y; vrow[gi][2] = r4.z; vrow[gi][3] = r4.w;
@@ -331,20 +339,19 @@ __global__ __launch_bounds__(256) void attn_kernel(
                 vrow[gi][0] = r2.x; vrow[gi][1] = r2.y;
             }
         }
+        // validity of the row this lane scores (row r16 of each group)
         uint32_t kvalid = 0;
 #pragma unroll
-        for (int gi = 0; gi < NGRP; ++gi) kvalid |= (krow[gi] >= 0 ? 1u : 0u) << gi;
+        for (int gi = 0; gi < NGRP; ++gi) kvalid |= (sw[16 * gi + r16] >= 0 ? 1u : 0u) << gi;
         // all loads in flight together, K then V of each group in turn, so the
-        // first group can start while the later ones arrive.  A K load takes 64 B of
-        // each of 16 rows, so two loads share every 128 B line: K is read with the
-        // default cache policy (the streaming hint made the second half-line miss;
-        // measured 0.6 us slower on a 128K-token step), V rows whole with the hint
-        uint4 kb[NGRP][KB], vr[NGRP][VL];
+        // first group can start while the later ones arrive
+        uint4 kr[NGRP][VL], vr[NGRP][VL];
 #pragma unroll
         for (int gi = 0; gi < NGRP; ++gi) {
-            const T *kr = kc + (size_t)(krow[gi] < 0 ? 0 : krow[gi]) * D + 8 * t4;
 #pragma unroll
-            for (int j = 0; j < KB; ++j) kb[gi][j] = *reinterpret_cast<const uint4 *>(kr + 32 * j);
+            for (int jj = 0; jj < VL; ++jj)
+                kr[gi][jj] = load_nt(kc + (size_t)(vrow[gi][jj] < 0 ? 0 : vrow[gi][jj]) * D +
+                                     ls * EPL);
 #pragma unroll
             for (int jj = 0; jj < VL; ++jj)
                 vr[gi][jj] = load_nt(vc + (size_t)(vrow[gi][jj] < 0 ? 0 : vrow[gi][jj]) * D +
@@ -352,15 +359,32 @@ __global__ __launch_bounds__(256) void attn_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
 
+        // swz(r): 16-byte slot rotation of tile row r (LPR slots per row)
+        constexpr int kSwzShift = LPR == 16 ? 0 : LPR == 8 ? 1 : -1;
+        static_assert(kSwzShift >= 0, "tile rows of 8 or 16 pieces");
+        uint4 *tile = reinterpret_cast<uint4 *>(s_big) + w * 16 * LPR;
         float *sp = s_p[w];
 #pragma unroll
         for (int gi = 0; gi < NGRP; ++gi) {
+            // K rows of the group through the tile
+#pragma unroll
+            for (int jj = 0; jj < VL; ++jj) {
+                const int r = rs * VL + jj;
+                tile[r * LPR + (ls ^ ((r >> kSwzShift) & (LPR - 1)))] = kr[gi][jj];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            uint4 kb[KB];
+#pragma unroll
+            for (int j = 0; j < KB; ++j)
+                kb[j] = tile[r16 * LPR + ((4 * j + t4) ^ ((r16 >> kSwzShift) & (LPR - 1)))];
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             // S[4*t4 + i][r16] = q_head . K_row over KB k-blocks
             f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < KB; ++j)
                 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    qa[j], __builtin_bit_cast(bf16x8_t, kb[gi][j]), c, 0, 0, 0);
+                    __builtin_bit_cast(bf16x8_t, s_q[(r16 % GH) * (D / 8) + 4 * j + t4]),
+                    __builtin_bit_cast(bf16x8_t, kb[j]), c, 0, 0, 0);
             const bool ok = (kvalid >> gi) & 1u;
             float z[4];
             bool need = false;
