@@ -8,8 +8,7 @@
 //   o_h = sum_{j in I_g} exp(z_j - max z) V_j / sum_{j in I_g} exp(z_j - max z),
 //   z_j = scale * q_h . K_j.
 //
-// gfx950 design (VALU path; per token the group's 4 heads need 2*4*d FMAs on
-// 2*d*2 bytes, ~2 FMA/B, below the fp32 vector ridge):
+// gfx950 design:
 // * grid = (NG, splits): the graph index varies fastest, so the workgroups of one
 //   graph share an XCD (and its L2) and the short last splits are dispatched last;
 //   a graph's list is cut into `nsplit` balanced chunks of <= CH entries.
@@ -18,15 +17,21 @@
 // * Phase B: a K or V row (d*elem bytes, 256 B for bf16 d=128) is read by LPR =
 //   row_bytes/16 lanes with one 16-byte load each, so a wave-wide load gathers
 //   64/LPR whole rows (1 KiB); every wave issues its 2*NLD loads back to back with
-//   no branches (rows of invalid entries point at row 0 and are masked).
-// * q.K: bf16 pairs go straight into v_dot2_f32_bf16 (exact bf16 products, fp32
-//   sums), partial sums are reduced over the LPR lanes of a row with DPP adds.
-//   Softmax runs online (one rescale per 2 loads) in the log2 domain in fp32, so
-//   no logits are kept and a lane holds only its 2*NLD loads, q and acc: with
-//   NLD = 12 the kernel fits 3 waves per SIMD and a 128K-token step's whole K/V
-//   working set is requested in one round of workgroups.  The wave's row slots and
-//   then the 4 waves are merged; the workgroup writes one partial (m, l, acc[d])
-//   per head.
+//   no branches (rows of invalid entries point at row 0 and are masked), so with
+//   NLD = 12 and 3 waves per SIMD a 128K-token step's whole K/V working set is
+//   requested in one round of workgroups.
+// * bf16 q.K on the matrix cores: the wave's rows form groups of 16.  A group's K
+//   rows pass through a per-wave LDS tile into the B operand of
+//   v_mfma_f32_16x16x32_bf16 (exact bf16 products, fp32 sums); the A operand
+//   repeats the graph's query heads down its 16 rows, so accumulator register i of
+//   lane (row r, quarter t) holds the logit of row r for head (4t + i) % GH.  Each
+//   (row, head) then takes one exp, and p reaches the lanes that hold the row's V
+//   pieces through LDS.  The wave keeps one softmax reference per head, rescaled
+//   lazily in the log2 domain; P.V is fp32 FMAs on the vector ALUs.
+// * fp32 rows: dot products over the LPR lanes of a row with DPP sums, online
+//   softmax per row slot.
+// * The wave's row slots and then the 4 waves are merged; the workgroup writes one
+//   partial (m, l, acc[d]) per head.
 // * The merge (next launch, so no device-wide fences are needed) combines the
 //   partials: m* = max m_s, l = sum l_s 2^(m_s-m*), o = sum acc_s 2^(m_s-m*) / l.
 // * In the fused decode step grid row 0 holds extra workgroups, one wave per
@@ -68,7 +73,6 @@ __device__ __forceinline__ int graph_of_column(int x, int NG, int gpk) {
     return x;
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -106,30 +110,8 @@ __device__ __forceinline__ float pair_op(float x, Op op) {
     }
 }
 
-// Partial q.K over this lane's EPL elements of a row, for one head.
-template <typename T, int EPL>
-__device__ __forceinline__ float qk_part(const uint32_t (&qp)[EPL / 2 > 0 ? EPL / 2 : 1],
-                                         const float (&qf)[EPL], const uint4 &k);
-
-template <>
-__device__ __forceinline__ float qk_part<bf16_t, 8>(const uint32_t (&qp)[4], const float (&)[8],
-                                                    const uint4 &k) {
-    // bf16 x bf16 products are exact in fp32; v_dot2 accumulates two per step
-    float s = 0.f;
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[0]),
-                                        __builtin_bit_cast(bf16x2_t, k.x), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[1]),
-                                        __builtin_bit_cast(bf16x2_t, k.y), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[2]),
-                                        __builtin_bit_cast(bf16x2_t, k.z), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[3]),
-                                        __builtin_bit_cast(bf16x2_t, k.w), s, false);
-    return s;
-}
-
-template <>
-__device__ __forceinline__ float qk_part<float, 4>(const uint32_t (&)[2], const float (&qf)[4],
-                                                   const uint4 &k) {
+// Partial q.K over this lane's 4 fp32 elements of a row, for one head.
+__device__ __forceinline__ float qk_part_f32(const float (&qf)[4], const uint4 &k) {
     float s = 0.f;
     s = fmaf(qf[0], __uint_as_float(k.x), s);
     s = fmaf(qf[1], __uint_as_float(k.y), s);
@@ -174,7 +156,6 @@ __global__ __launch_bounds__(256) void attn_kernel(
     constexpr int NLD = kAttnLoads;         // loads per wave for K (and for V)
     constexpr int TPW = NLD * RPW;          // tokens per wave
     constexpr int CH = TPW * kAttnWaves;    // tokens per workgroup (max)
-    constexpr int NQP = EPL / 2 > 0 ? EPL / 2 : 1;
     constexpr int kSub = 2;                 // loads per online-softmax batch
     static_assert(CH == attn_chunk(D, sizeof(T)), "chunk");
     static_assert(LPR >= 1 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "row split");
@@ -246,8 +227,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
     // products on the vector ALUs (below)
     const int r16 = lane & 15, t4 = lane >> 4;  // matrix-core lane coordinates
 
-    // query slice: packed bf16 pairs (dot2) or fp32; the scale is applied to the sum
-    uint32_t qp[GH][NQP];
+    // fp32 query slice of this lane; the scale is applied to the sum
     float qf[GH][EPL];
     // matrix-core A operand (bf16): row r16 is head r16 % GH (the heads repeat down
     // the 16 rows), k-block j of 32 elements, this lane's 8 at 32j + 8*t4.  The GH
@@ -499,7 +479,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
         for (int j = 0; j < kSub; ++j) {
 #pragma unroll
             for (int h = 0; h < GH; ++h) {
-                const float s = group_sum<LPR>(qk_part<T, EPL>(qp[h], qf[h], kr[i0 + j]));
+                const float s = group_sum<LPR>(qk_part_f32(qf[h], kr[i0 + j]));
                 z[j][h] = (valid >> (i0 + j)) & 1u ? s * scale_log2 : -__builtin_inff();
             }
         }
