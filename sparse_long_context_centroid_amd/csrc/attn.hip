@@ -167,9 +167,9 @@ __global__ __launch_bounds__(256) void attn_kernel(
     __shared__ float s_l[kAttnWaves][GH];
     __shared__ float s_acc[kAttnWaves][GH][D];
     __shared__ __align__(16) float s_p[kAttnWaves][16 * GH];  // bf16 path: p of one group
-    // bf16 path: per wave, the K rows of one 16-row group (16 x D bf16), shared with
-    // the fused update's rows (grid row 0 runs only the update)
-    // plus the graph's GH query rows (bf16) after the tiles
+    // s_big, bf16 path: one tile per wave for the K rows of a 16-row group (16 x D
+    // bf16), then the graph's GH query rows (bf16).  In the fused step, grid row 0
+    // runs only the local update and uses the same memory for its candidate rows.
     constexpr int kStageFloats = kMfma ? kAttnWaves * 16 * D / 2 + GH * D / 2 : 1;
     constexpr int kUpdFloats = MODE == kAttnIndexedUpdate ? kAttnWaves * kUpdLdsFloats(D) : 1;
     __shared__ __align__(16) float s_big[kStageFloats > kUpdFloats ? kStageFloats : kUpdFloats];
