@@ -13,6 +13,7 @@
 // workgroup widens the graph's queries to fp64 in LDS, [d/4][GH][4], so the
 // per-element query values are wave-uniform broadcast reads.
 #include <type_traits>
+#include <utility>
 
 #include "ckv_device.h"
 #include "ckv_internal.h"
@@ -26,9 +27,47 @@ constexpr int kScoreThreads = 64;
 // issued before the current one is consumed (two chunks of registers).
 constexpr int kScoreChunk = 8;
 
+// v_fmac_f64 whose first factor comes from lane N of this lane's 16-lane row (DPP
+// row_newbcast, a gfx90a+ 64-bit DPP control): acc = q[row lane N] * m + acc with
+// one rounding, exactly as fma().  q must not be written by a VALU instruction in
+// the two instructions before (the DPP read hazard; the compiler does not look
+// inside inline asm): callers load q from LDS and issue s_nop 1 first.
+template <int N>
+__device__ __forceinline__ void fmac_row_bcast(double &acc, double q, double m) {
+    asm volatile("v_fmac_f64_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(acc)
+                 : "v"(q), "v"(m), "n"(N));
+}
+
+// The FMAs of float4 step KK of a chunk, in element order and, per element, head
+// order: query value v = (4*KK + c)*GH + h of the chunk sits in register v / 16 at
+// row lane v % 16.
+template <int GH, int NRP, int KK, int I>
+__device__ __forceinline__ void score_fma(double (&acc)[GH], const double (&qr)[NRP],
+                                          const double (&e)[4]) {
+    constexpr int c = I / GH, h = I % GH, v = (4 * KK + c) * GH + h;
+    fmac_row_bcast<v % 16>(acc[h], qr[v / 16], e[c]);
+}
+template <int GH, int NRP, int KK, int... I>
+__device__ __forceinline__ void score_step(double (&acc)[GH], const double (&qr)[NRP],
+                                           const float4 &f, std::integer_sequence<int, I...>) {
+    const double e[4] = {f.x, f.y, f.z, f.w};
+    asm volatile("s_nop 1");
+    (score_fma<GH, NRP, KK, I>(acc, qr, e), ...);
+}
+template <int GH, int NRP, int KC, int... KK>
+__device__ __forceinline__ void score_chunk(double (&acc)[GH], const double (&qr)[NRP],
+                                            const float4 (&cur)[KC],
+                                            std::integer_sequence<int, KK...>) {
+    (score_step<GH, NRP, KK>(acc, qr, cur[KK], std::make_integer_sequence<int, 4 * GH>{}), ...);
+}
+
 // One workgroup = 64 consecutive communities of one graph, one per lane.  The
-// graph's GH query rows are widened to fp64 once into LDS, laid out [d/4][GH][4]
-// so that each step's 4*GH values are one contiguous broadcast read.
+// graph's GH query rows are widened to fp64 once into LDS, in value order
+// v = element*GH + head.  Per chunk of 4*KC elements each lane fetches 4*KC*GH/16
+// of the chunk's values (lane p of a 16-lane row: values p, 16 + p, ...), and the
+// FMAs take each value from its row lane with a DPP broadcast: the chunk costs a
+// few LDS reads per lane instead of one broadcast LDS read per value.
 template <typename T, int D, int GH>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const T *__restrict__ q, const float *__restrict__ cent, const int32_t *__restrict__ num_comms,
@@ -36,10 +75,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     float *__restrict__ scores) {
     constexpr int KC = kScoreChunk;
     static_assert((D / 4) % KC == 0, "whole chunks");
-    // lane j stages entries 4j..4j+3 of [d/4][GH][4]: elements 4k..4k+3 of head h,
-    // k = j / GH, h = j % GH, with one vector load
+    // lane j stages elements 4k..4k+3 of head h, k = j / GH, h = j % GH, with one
+    // vector load
     constexpr int NQ = (D * GH / 4 + kScoreThreads - 1) / kScoreThreads;
-    __shared__ double sq[NQ * kScoreThreads * 4];
+    constexpr int NRP = 4 * KC * GH / 16;  // query registers per lane per chunk
+    static_assert((4 * KC * GH) % 16 == 0, "whole 16-lane rows of query values");
+    __shared__ double sq[D * GH];
     const int g = blockIdx.y;
     const int c0 = blockIdx.x * kScoreThreads + threadIdx.x;
     const int c = min(c0, Cmax - 1);
@@ -82,8 +123,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
             e4[2] = w.z;
             e4[3] = w.w;
         }
+        const int jq = min((int)threadIdx.x + j * kScoreThreads, D * GH / 4 - 1);
+        const int k = jq / GH, h = jq % GH;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sq[(threadIdx.x + j * kScoreThreads) * 4 + e] = (double)e4[e];
+        for (int e = 0; e < 4; ++e) sq[(4 * k + e) * GH + h] = (double)e4[e];
     }
     __syncthreads();
 
@@ -98,19 +141,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
         const int kn = min(k0 + KC, D / 4 - KC);  // the last pass reloads a chunk, unused
 #pragma unroll
         for (int k = 0; k < KC; ++k) nxt[k] = cp[(size_t)(kn + k) * Cmax];
+        double qr[NRP];
+        const double *qc = sq + 4 * k0 * GH + (threadIdx.x & 15);
 #pragma unroll
-        for (int kk = 0; kk < KC; ++kk) {
-            const int k = k0 + kk;
-            const double e0 = cur[kk].x, e1 = cur[kk].y, e2 = cur[kk].z, e3 = cur[kk].w;
-#pragma unroll
-            for (int h = 0; h < GH; ++h) {
-                const double *qq = sq + (k * GH + h) * 4;
-                acc[h] = fma(qq[0], e0, acc[h]);
-                acc[h] = fma(qq[1], e1, acc[h]);
-                acc[h] = fma(qq[2], e2, acc[h]);
-                acc[h] = fma(qq[3], e3, acc[h]);
-            }
-        }
+        for (int j = 0; j < NRP; ++j) qr[j] = qc[16 * j];
+        score_chunk<GH, NRP, KC>(acc, qr, cur, std::make_integer_sequence<int, KC>{});
 #pragma unroll
         for (int k = 0; k < KC; ++k) cur[k] = nxt[k];
     }
