@@ -174,7 +174,9 @@ __global__ __launch_bounds__(kLayerScoreWaves * kWave) void layer_score_kernel(
     constexpr int KC = kScoreChunk;
     static_assert((D / 4) % KC == 0, "whole chunks");
     constexpr int NQ = (D * GH / 4 + kWave - 1) / kWave;
-    __shared__ double sq[kLayerScoreWaves][NQ * kWave * 4];
+    constexpr int NRP = 4 * KC * GH / 16;  // query registers per lane per chunk
+    static_assert((4 * KC * GH) % 16 == 0, "whole 16-lane rows of query values");
+    __shared__ double sq[kLayerScoreWaves][D * GH];
     __shared__ float s_best[kLayerScoreWaves][kWave];
     const int b = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
@@ -220,8 +222,10 @@ __global__ __launch_bounds__(kLayerScoreWaves * kWave) void layer_score_kernel(
                 e4[2] = wv.z;
                 e4[3] = wv.w;
             }
+            const int jq = min(lane + j * kWave, D * GH / 4 - 1);
+            const int k = jq / GH, h = jq % GH;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sqw[(lane + j * kWave) * 4 + e] = (double)e4[e];
+            for (int e = 0; e < 4; ++e) sqw[(4 * k + e) * GH + h] = (double)e4[e];
         }
         __builtin_amdgcn_wave_barrier();
         double acc[GH];
@@ -233,19 +237,11 @@ __global__ __launch_bounds__(kLayerScoreWaves * kWave) void layer_score_kernel(
             const int kn = min(k0 + KC, D / 4 - KC);
 #pragma unroll
             for (int k = 0; k < KC; ++k) nxt[k] = cp[(size_t)(kn + k) * Cmax];
+            double qr[NRP];
+            const double *qc = sqw + 4 * k0 * GH + (lane & 15);
 #pragma unroll
-            for (int kk = 0; kk < KC; ++kk) {
-                const int k = k0 + kk;
-                const double e0 = cur[kk].x, e1 = cur[kk].y, e2 = cur[kk].z, e3 = cur[kk].w;
-#pragma unroll
-                for (int h = 0; h < GH; ++h) {
-                    const double *qq = sqw + (k * GH + h) * 4;
-                    acc[h] = fma(qq[0], e0, acc[h]);
-                    acc[h] = fma(qq[1], e1, acc[h]);
-                    acc[h] = fma(qq[2], e2, acc[h]);
-                    acc[h] = fma(qq[3], e3, acc[h]);
-                }
-            }
+            for (int j = 0; j < NRP; ++j) qr[j] = qc[16 * j];
+            score_chunk<GH, NRP, KC>(acc, qr, cur, std::make_integer_sequence<int, KC>{});
 #pragma unroll
             for (int k = 0; k < KC; ++k) cur[k] = nxt[k];
         }
