@@ -325,16 +325,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             // crossing (unit weights)
             const int4 *pend = w == 0 ? pendA : pendB;
             const int np = w == 0 ? nPA : nPB;
+            // one entry per lane (np <= kPend = kWave); the others arrive by readlane
+            const int4 me = pend[lane < np ? lane : 0];
+            const uint32_t k0 = (uint32_t)me.x;
+            int before = 0;
+            for (int j = 0; j < np; ++j) {
+                const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane(me.x, j);
+                const int ij = __builtin_amdgcn_readlane(me.y, j);
+                const int wj = __builtin_amdgcn_readlane(me.z, j);
+                before += (kj > k0 || (kj == k0 && ij < me.y)) ? wj : 0;
+            }
             if (lane < np) {
-                const int4 me = pend[lane];
-                const uint32_t k0 = (uint32_t)me.x;
-                int before = 0;
-#pragma unroll 4
-                for (int j = 0; j < np; ++j) {
-                    const int4 o = pend[j];
-                    const uint32_t kj = (uint32_t)o.x;
-                    before += (kj > k0 || (kj == k0 && o.y < me.y)) ? o.z : 0;
-                }
                 if (w == 0) pendA_sel[lane] = aboveA_b + before + me.z <= Bt;
                 else pendB_sel[lane] = aboveB_b + before + 1 <= M;
             }
@@ -436,20 +437,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         if (selected && c < Cmax) selected[(size_t)g * Cmax + c] = selA[i] ? 1 : 0;
     }
     if (tid == 0) list_off[ksel] = total;
-    if (tid < M) {
+    if (w == 0) {
         // the candidates (at most M <= CKV_MAX_CAND, unordered in LDS) go out in
-        // (key desc, id asc) order: each one's rank is the number it yields to
+        // (key desc, id asc) order: each one's rank is the number it yields to; one
+        // candidate per lane, the others compared through readlane
         const int nc = cand_n < M ? cand_n : M;
-        if (tid < nc) {
-            const uint32_t kk = cand_key[tid];
-            const int ii = cand_id[tid];
-            int r = 0;
-            for (int j = 0; j < nc; ++j)
-                r += (cand_key[j] > kk || (cand_key[j] == kk && cand_id[j] < ii)) ? 1 : 0;
-            cand[(size_t)g * M + r] = ii;
-        } else {
-            cand[(size_t)g * M + tid] = -1;
+        const uint32_t kk = cand_key[lane < nc ? lane : 0];
+        const int ii = cand_id[lane < nc ? lane : 0];
+        int r = 0;
+        for (int j = 0; j < nc; ++j) {
+            const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)kk, j);
+            const int ij = __builtin_amdgcn_readlane(ii, j);
+            r += (kj > kk || (kj == kk && ij < ii)) ? 1 : 0;
         }
+        if (lane < nc) cand[(size_t)g * M + r] = ii;
+        else if (lane < M) cand[(size_t)g * M + lane] = -1;
     }
     __syncthreads();
 
