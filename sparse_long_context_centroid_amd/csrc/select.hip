@@ -333,7 +333,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane(me.x, j);
                 const int ij = __builtin_amdgcn_readlane(me.y, j);
                 const int wj = __builtin_amdgcn_readlane(me.z, j);
-                before += (kj > k0 || (kj == k0 && ij < me.y)) ? wj : 0;
+                // bitwise, not short-circuit: the loop stays free of branches
+                before += ((kj > k0) | ((kj == k0) & (ij < me.y))) ? wj : 0;
             }
             if (lane < np) {
                 if (w == 0) pendA_sel[lane] = aboveA_b + before + me.z <= Bt;
@@ -448,7 +449,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         for (int j = 0; j < nc; ++j) {
             const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)kk, j);
             const int ij = __builtin_amdgcn_readlane(ii, j);
-            r += (kj > kk || (kj == kk && ij < ii)) ? 1 : 0;
+            r += ((kj > kk) | ((kj == kk) & (ij < ii))) ? 1 : 0;
         }
         if (lane < nc) cand[(size_t)g * M + r] = ii;
         else if (lane < M) cand[(size_t)g * M + lane] = -1;
