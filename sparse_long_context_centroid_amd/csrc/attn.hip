@@ -665,9 +665,11 @@ __device__ __forceinline__ void merge_graph(int g, int Hq, int Hkv, int gpk,
     const int t0 = tid < GH * D ? tid : 0;
     const int h = t0 / D, i = t0 % D;
     const float *pa = pbase + (size_t)h * max_splits * (D + 2) + 2 + i;
+    // loads at clamped slots, unconditionally: a load inside a branch would make the
+    // compiler wait for each one in turn
     float x[kBatch];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) x[k] = k < max_splits ? pa[(size_t)k * (D + 2)] : 0.f;
+    for (int k = 0; k < kBatch; ++k) x[k] = pa[(size_t)min(k, max_splits - 1) * (D + 2)];
     // weights: one wave per head
     for (int hh = w; hh < GH; hh += blockDim.x / kWave) {
         const float *ph = pbase + (size_t)hh * max_splits * (D + 2);
@@ -708,14 +710,16 @@ __device__ __forceinline__ void merge_graph(int g, int Hq, int Hkv, int gpk,
             if (s0 > 0 || t != tid) {
 #pragma unroll
                 for (int k = 0; k < kBatch; ++k)
-                    x[k] = s0 + k < max_splits ? pt[(size_t)(s0 + k) * (D + 2)] : 0.f;
+                    x[k] = pt[(size_t)min(s0 + k, max_splits - 1) * (D + 2)];
             }
+            // weight 0 (an empty split, or a slot past the last) contributes nothing,
+            // whatever its never-written acc holds; selects, no branches
 #pragma unroll
             for (int k = 0; k < kBatch; ++k) {
-                if (s0 + k < max_splits) {
-                    const float wk = s_w[ht * max_splits + s0 + k];
-                    if (wk != 0.f) a += x[k] * wk;
-                }
+                const float wk = s_w[ht * max_splits + min(s0 + k, max_splits - 1)];
+                const bool use = (s0 + k < max_splits) & (wk != 0.f);
+                const float term = x[k] * wk;
+                a += use ? term : 0.f;
             }
         }
         out[((size_t)b * Hq + h0 + ht) * D + it] = a;
