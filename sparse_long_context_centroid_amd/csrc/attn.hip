@@ -275,23 +275,20 @@ __global__ __launch_bounds__(256) void attn_kernel(
     // this wave, folded into the running state
     auto chunk = [&](const int c0, const int c_end) {
     // ---- phase A: list entries -> row indices in LDS
+    // both loads at clamped slots, unconditionally (a load under a branch makes the
+    // compiler wait for it there); validity is decided by selects afterwards.
+    // c0 < c_end <= idx_stride, so the clamped list slot is always in the list.
     for (int t = tid; t < CH; t += blockDim.x) {
         const int te = c0 + t;
-        int row = -1;
-        if (te < c_end) {
-            const int pos = MODE == kAttnDense ? te : idx[(size_t)gl * idx_stride + te];
-            if (pos >= 0 && pos < n) {
-                const int lp = pos >> log2ps;
-                const int pg = lp < max_pages ? page_table[(size_t)b * max_pages + lp] : -1;
-                if (pg >= 0 && pg < num_pages)
-                    row = ((pg * Hkv + kvh) << log2ps) + (pos & ((1 << log2ps) - 1));
-                else
-                    set_err(err, CKV_DEVERR_UNMAPPED_PAGE);
-            } else {
-                set_err(err, CKV_DEVERR_INDEX_RANGE);
-            }
-        }
-        s_row[t] = row;
+        const bool in = te < c_end;
+        const int pos = MODE == kAttnDense ? te : idx[(size_t)gl * idx_stride + min(te, c_end - 1)];
+        const bool pos_ok = in & (pos >= 0) & (pos < n);
+        const int lp = pos_ok ? pos >> log2ps : 0;
+        const int pg = page_table[(size_t)b * max_pages + min(lp, max_pages - 1)];
+        const bool pg_ok = pos_ok & (lp < max_pages) & (pg >= 0) & (pg < num_pages);
+        s_row[t] = pg_ok ? ((pg * Hkv + kvh) << log2ps) + (pos & ((1 << log2ps) - 1)) : -1;
+        if (in & !pos_ok) set_err(err, CKV_DEVERR_INDEX_RANGE);
+        if (pos_ok & !pg_ok) set_err(err, CKV_DEVERR_UNMAPPED_PAGE);
     }
     __syncthreads();
 
