@@ -26,8 +26,12 @@
 //   repeats the graph's query heads down its 16 rows, so accumulator register i of
 //   lane (row r, quarter t) holds the logit of row r for head (4t + i) % GH.  Each
 //   (row, head) then takes one exp, and p reaches the lanes that hold the row's V
-//   pieces through LDS.  The wave keeps one softmax reference per head, rescaled
-//   lazily in the log2 domain; P.V is fp32 FMAs on the vector ALUs.
+//   pieces through LDS.  For d = 128 and up to 4 heads the operands are swapped:
+//   the output is indexed (row, head), lane (quarter t, column c) holds rows 4t+i
+//   for head c % GH -- the rows whose V pieces the lane reads -- and lane h of each
+//   quad holds head h, so p reaches the FMAs by a DPP quad broadcast, not LDS.  The
+//   wave keeps one softmax reference per head, rescaled lazily in the log2 domain;
+//   P.V is fp32 FMAs on the vector ALUs.
 // * fp32 rows: dot products over the LPR lanes of a row with DPP sums, online
 //   softmax per row slot.
 // * The wave's row slots and then the 4 waves are merged; the workgroup writes one
@@ -75,6 +79,16 @@ __device__ __forceinline__ int graph_of_column(int x, int NG, int gpk) {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Value of lane H of this lane's quad (DPP quad_perm [H,H,H,H]).
+__device__ __forceinline__ float quad_bcast(float x, int h) {
+    switch (h) {
+        case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x00, 0xF, 0xF, false));
+        case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x55, 0xF, 0xF, false));
+        case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xAA, 0xF, 0xF, false));
+        default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xFF, 0xF, 0xF, false));
+    }
+}
 
 // Maximum over the 16 lanes of a row, in every lane of the row.
 __device__ __forceinline__ float row_max16(float x) {
@@ -162,6 +176,9 @@ __global__ __launch_bounds__(256) void attn_kernel(
     static_assert(NLD % 4 == 0 && NLD % kSub == 0, "row slots are read as int4");
 
     constexpr bool kMfma = sizeof(T) == 2;  // bf16: q.K on the matrix cores
+    // bf16, d = 128, up to 4 heads: the MFMA output is indexed (row, head), so a lane
+    // holds the logits of the 4 rows whose V pieces it reads
+    constexpr bool kSwap = kMfma && D == 128 && GH <= 4;
     __shared__ __align__(16) int s_row[CH];
     __shared__ float s_m[kAttnWaves][GH];
     __shared__ float s_l[kAttnWaves][GH];
@@ -256,6 +273,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
     // domain), and lane partial sums of p; register i of a lane serves head
     // (4*t4 + i) % GH, the head of accumulator row 4*t4 + i
     float mv[4], thr[4], lsum[4];
+    float mv0 = -__FLT_MAX__, thr0 = -__FLT_MAX__, lsum0 = 0.f;  // swap layout: one head per lane
     constexpr float kLazy = 8.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -320,6 +338,15 @@ __global__ __launch_bounds__(256) void attn_kernel(
         uint32_t kvalid = 0;
 #pragma unroll
         for (int gi = 0; gi < NGRP; ++gi) kvalid |= (sw[16 * gi + r16] >= 0 ? 1u : 0u) << gi;
+        uint32_t rvalid = 0;  // swap layout: rows 4*t4 .. 4*t4+3 of each group
+        if constexpr (kSwap) {
+#pragma unroll
+            for (int gi = 0; gi < NGRP; ++gi) {
+                const int4 r4 = *reinterpret_cast<const int4 *>(sw + 16 * gi + 4 * t4);
+                rvalid |= ((r4.x >= 0 ? 1u : 0u) | (r4.y >= 0 ? 2u : 0u) | (r4.z >= 0 ? 4u : 0u) |
+                           (r4.w >= 0 ? 8u : 0u)) << (4 * gi);
+            }
+        }
         // all loads in flight together, K then V of each group in turn, so the
         // first group can start while the later ones arrive
         uint4 kr[NGRP][VL], vr[NGRP][VL];
@@ -355,6 +382,62 @@ __global__ __launch_bounds__(256) void attn_kernel(
             for (int j = 0; j < KB; ++j)
                 kb[j] = tile[r16 * LPR + ((4 * j + t4) ^ ((r16 >> kSwzShift) & (LPR - 1)))];
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if constexpr (kSwap) {
+                // C[row][col] = K_row . q_{col % GH}: lane (t4, r16) gets rows 4*t4 + i
+                // for head r16 % GH; the heads repeat every 4 columns, so lane j of each
+                // quad holds head j
+                f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < KB; ++j)
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, kb[j]),
+                        __builtin_bit_cast(bf16x8_t, s_q[(r16 % GH) * (D / 8) + 4 * j + t4]), c,
+                        0, 0, 0);
+                float z[4];
+                bool need = false;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    z[i] = (rvalid >> (4 * gi + i)) & 1u ? c[i] * scale_log2 : -__builtin_inff();
+                    need |= z[i] > thr0;
+                }
+                if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                    // this head's maximum over the 16 rows: the lane's 4, then the 4 quarters
+                    float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+                    mx = pair_op<16>(mx, OpMax{});
+                    mx = pair_op<32>(mx, OpMax{});
+                    const float mn = fmaxf(mv0, mx);
+                    const float cf = fast_exp2(mv0 - mn);
+                    mv0 = mn;
+                    thr0 = mn + kLazy;
+                    lsum0 *= cf;
+#pragma unroll
+                    for (int h = 0; h < GH; ++h) {
+                        const float f = GH == 1 ? cf : quad_bcast(cf, h);
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc[h][e] *= f;
+                    }
+                }
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = fast_exp2(z[i] - mv0);
+                    lsum0 += p[i];
+                }
+                // V lane (t4, ls) reads rows 4*t4 + jj: the rows of p[jj]; head h's weight
+                // comes from lane h of the lane's quad
+#pragma unroll
+                for (int jj = 0; jj < VL; ++jj) {
+                    float x[EPL];
+                    unpack<T, EPL>(vr[gi][jj], x);
+#pragma unroll
+                    for (int h = 0; h < GH; ++h) {
+                        const float ph = GH == 1 ? p[jj] : quad_bcast(p[jj], h);
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(ph, x[e], acc[h][e]);
+                    }
+                }
+                continue;
+            }
             // S[4*t4 + i][r16] = q_head . K_row over KB k-blocks
             f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -567,6 +650,15 @@ __global__ __launch_bounds__(256) void attn_kernel(
         float lt[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) lt[i] = group_sum<16>(lsum[i]);
+        if constexpr (kSwap) {
+            // l of head r16 % GH: the lane's rows, then the 4 quarters
+            float l0 = pair_op<16>(lsum0, OpAdd{});
+            l0 = pair_op<32>(l0, OpAdd{});
+            if (t4 == 0 && r16 < GH) {
+                s_m[w][r16] = mv0;
+                s_l[w][r16] = l0;
+            }
+        } else
         // lane 0 holds heads 0..min(GH,4)-1, lane 16 heads 4-7
         if (r16 == 0 && t4 < (GH > 4 ? 2 : 1)) {
 #pragma unroll
