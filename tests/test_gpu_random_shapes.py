@@ -3,8 +3,11 @@ the fp64 oracle: graph granularity (per KV head, per query head, per layer),
 dtype, head_dim, group size, batch with ragged contexts, shuffled pages, sink
 count, budget (0, small, beyond the context), candidate count and steps are drawn
 per case; both the four calls and the fused step are exercised.  Every case
-prints its parameters before it runs."""
+prints its parameters before it runs.  CKV_RANDOM_CASES sets the number of cases
+(256 by default; a longer sweep draws the same first 256 and more)."""
 from __future__ import annotations
+
+import os
 
 import numpy as np
 import pytest
@@ -16,7 +19,7 @@ from sparse_long_context_centroid_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 64
+N_CASES = int(os.environ.get("CKV_RANDOM_CASES", "256"))
 
 
 @pytest.fixture(scope="module", autouse=True)
