@@ -105,8 +105,9 @@ typedef struct ckv_dims {
  * at elements kvh*d .. kvh*d+d-1); its score is the max over all query heads of
  * q_h . (head kvh(h)'s centroid) * scale; one index list serves every KV head;
  * the new token's key row (its Hkv keys, in order) joins the nearest candidate in
- * squared L2 over the whole row, accumulated per KV head (each head's slice in
- * fp64 in element order, then the slices in head order), and every KV head's K/V
+ * squared L2 over the whole row (fp64; the kernel sums each KV head's slice in
+ * element order, then the slices in head order -- an order that can only swap
+ * candidates whose distances agree to within rounding), and every KV head's K/V
  * row n is written.  The layer graph's update stages M centroid rows in LDS:
  * Hkv <= 32, Hkv*d <= 4096 and M*(Hkv*d+4)*4 + Hkv*d*8 bytes within 64 KiB, else
  * CKV_ERR_UNSUPPORTED.  ckv_prefill_edges does not
@@ -124,7 +125,9 @@ typedef struct ckv_graphs {
     int32_t *comm_start; /* [NG*Cmax]                                                 */
     int32_t *comm_size;  /* [NG*Cmax]                                                 */
     int32_t *comm_cap;   /* [NG*Cmax]                                                 */
-    int32_t *members;    /* member pool (token positions)                            */
+    int32_t *members;    /* member pool (token positions); NULL allowed only for an
+                            empty pool: every comm_cap of every graph is 0 (e.g.
+                            every sequence holds sinks only)                        */
 } ckv_graphs;
 
 /* Full, never-evicted paged KV cache of one layer. */

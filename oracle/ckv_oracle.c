@@ -253,10 +253,10 @@ int ckvo_update(int d, const void *k_new, int dtype, const int32_t *cand, int n_
  * The update of a whole-layer graph [RIT-granul, RIT-plan: one graph may serve a
  * whole layer].  A centroid row is nseg slices of d values, one slice per KV head
  * (row length nseg*d), and k_new is the matching row of the new token's keys.
- * Reading: the distance of a candidate is the squared L2 distance over the row,
- * accumulated per KV head -- each slice's sum in fp64 in element order, then the
- * slices' sums added in slice order; lower id on equal distance.  The winner's
- * whole row moves to the running mean, exactly as in ckvo_update.
+ * Reading: the new token is one node of the one graph, so the distance of a
+ * candidate is the plain squared L2 distance over the whole row -- one fp64 sum
+ * over all nseg*d elements in element order; lower id on equal distance.  The
+ * winner's whole row moves to the running mean, exactly as in ckvo_update.
  */
 int ckvo_update_layer(int d, int nseg, const void *k_new, int dtype, const int32_t *cand,
                       int n_cand, float *cent, int32_t *size, const int32_t *cap,
@@ -268,14 +268,9 @@ int ckvo_update_layer(int d, int nseg, const void *k_new, int dtype, const int32
     for (int m = 0; m < n_cand; ++m) {
         const int c = cand[m];
         double total = 0.0;
-        for (int sg = 0; sg < nseg; ++sg) {
-            double part = 0.0;
-            for (int i = 0; i < d; ++i) {
-                long e = (long)sg * d + i;
-                const double gap = widen(k_new, e, dtype) - (double)cent[(long)c * row + e];
-                part = part + gap * gap;
-            }
-            total = total + part;
+        for (long e = 0; e < row; ++e) {
+            const double gap = widen(k_new, e, dtype) - (double)cent[(long)c * row + e];
+            total = total + gap * gap;
         }
         if (total < win_dist || (total == win_dist && c < win)) {
             win_dist = total;
@@ -420,4 +415,50 @@ void ckvo_edges(int d, int G, const void *Q, const void *K, int dtype, int S, fl
         }
         free(z);
     }
+}
+
+/*
+ * Co-attention edges of the prefill token graph [RIT-graph: besides the direct
+ * query->key links, the graph links keys that are attended together; abstract:
+ * the token graph is built from the prefill's QK^T scores].  Readings: two keys
+ * are attended together when both are among one query's `topk` strongest keys
+ * (the direct edges of ckvo_edges); every such pair is emitted once per query,
+ * unaggregated, as (lower position, higher position).  The valid keys of a row
+ * are sorted ascending, a[0] < a[1] < ... < a[cnt-1]; the pair slots of a row are
+ * the index pairs (x, y), 0 <= x < y < topk, in lexicographic order, and slot
+ * (x, y) holds (a[x], a[y]) when y < cnt, else (-1, -1).
+ *
+ *   idx   : [nrows][topk] key positions, -1 where a query has fewer keys
+ *   pairs : [nrows][topk*(topk-1)/2][2]
+ */
+void ckvo_coattention_pairs(int topk, const int32_t *idx, int nrows, int32_t *pairs)
+{
+    int32_t *keys = (int32_t *)malloc(sizeof(int32_t) * (size_t)(topk > 0 ? topk : 1));
+    const long per_row = (long)topk * (topk - 1) / 2;
+    for (int r = 0; r < nrows; ++r) {
+        int cnt = 0;
+        for (int t = 0; t < topk; ++t) {
+            int32_t j = idx[(long)r * topk + t];
+            if (j < 0)
+                continue;
+            /* insertion into the ascending list of the row's keys */
+            int at = cnt;
+            while (at > 0 && keys[at - 1] > j) {
+                keys[at] = keys[at - 1];
+                --at;
+            }
+            keys[at] = j;
+            ++cnt;
+        }
+        int32_t *out = pairs + (long)r * per_row * 2;
+        long slot = 0;
+        for (int x = 0; x < topk; ++x) {
+            for (int y = x + 1; y < topk; ++y) {
+                out[2 * slot] = y < cnt ? keys[x] : -1;
+                out[2 * slot + 1] = y < cnt ? keys[y] : -1;
+                ++slot;
+            }
+        }
+    }
+    free(keys);
 }

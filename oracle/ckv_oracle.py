@@ -23,9 +23,8 @@ mean of its members' keys in that head), stored as one row of Hkv*d values,
 KV head after KV head; its score is the max over all query heads of
 q_h . mu_{c, kv head of h} * scale (the group reading, over the whole layer);
 one index list serves every KV head; the new token joins the nearest candidate
-in squared L2 over the whole row (all KV heads' keys), accumulated per KV head:
-each head's slice summed in element order, then the slices in head order
-(ckvo_update_layer).
+in squared L2 over the whole row (all KV heads' keys), one fp64 sum over the
+row in element order (ckvo_update_layer).
 """
 from __future__ import annotations
 
@@ -91,6 +90,8 @@ def lib():
             L.ckvo_edge_scores.restype = None
             L.ckvo_update_layer.argtypes = [i32, i32, P, i32, P, i32, P, P, P, P, P, i32]
             L.ckvo_update_layer.restype = i32
+            L.ckvo_coattention_pairs.argtypes = [i32, P, i32, P]
+            L.ckvo_coattention_pairs.restype = None
             _lib = L
     return _lib
 
@@ -216,6 +217,17 @@ def edges(Q: np.ndarray, K: np.ndarray, S: int, scale: float, topk: int, rows=No
     return idx, score
 
 
+def coattention_pairs(idx: np.ndarray, topk: int) -> np.ndarray:
+    """idx [rows, topk] direct-edge key positions (-1 padded) -> co-attention pairs
+    [rows, topk*(topk-1)/2, 2]: every pair of a row's keys, (lower, higher)."""
+    idx = np.ascontiguousarray(idx, np.int32).reshape(-1, topk)
+    npair = topk * (topk - 1) // 2
+    out = np.empty((idx.shape[0], npair, 2), np.int32)
+    if npair and idx.shape[0]:
+        lib().ckvo_coattention_pairs(int(topk), _p(idx), idx.shape[0], _p(out))
+    return out
+
+
 def update_layer(k_new: np.ndarray, cand: np.ndarray, cent: np.ndarray, size: np.ndarray,
                  cap: np.ndarray, start: np.ndarray, members: np.ndarray, n: int, nseg: int):
     """The layer graph's update: rows of nseg slices (one per KV head); in place
@@ -272,6 +284,29 @@ class OracleState:
         self.V = np.array(V, copy=True, order="C")
         self.seq_len = np.array(seq_len, np.int32, copy=True)
         self.threads = threads or len(os.sched_getaffinity(0))
+        self._layer_undo = {}
+
+    def layer_candidate_rows(self, g: int):
+        """Layer graph g: (candidate ids, their centroid rows before the last step's
+        update, the new token's key row) of the last step."""
+        before, cand, krow, _ = self._layer_undo[g]
+        return cand, (before[0] if before is not None else None), krow
+
+    def adopt_layer_choice(self, g: int, c: int):
+        """Replace the last step's layer-graph choice of graph g by community c (one
+        of its candidates): the state goes back to before that update, then the
+        update runs with c as the only candidate.  -> the new result code."""
+        before, cand, krow, n = self._layer_undo[g]
+        assert before is not None and c in set(int(x) for x in cand)
+        rows, size, slots, vals = before
+        self.cent[g, cand] = rows
+        self.size[g, cand] = size
+        ok = slots >= 0
+        self.members[slots[ok]] = vals[ok]
+        Cn = int(self.num_comms[g])
+        return update_layer(krow, np.array([c], np.int32), self.cent[g, :Cn],
+                            self.size[g, :Cn], self.cap[g, :Cn], self.start[g, :Cn],
+                            self.members, n, self.Hkv)
 
     def heads_of(self, g: int):
         if self.layer:
@@ -301,9 +336,18 @@ class OracleState:
         for kvh in range(self.Hkv):
             for h in range(kvh * G, (kvh + 1) * G):
                 outs[h] = attend(q[b, h], self.K[b, kvh], self.V[b, kvh], idx, scale)
-        r = update_layer(np.ascontiguousarray(k_new[b]).reshape(-1), cand, self.cent[g, :Cn],
-                         self.size[g, :Cn], self.cap[g, :Cn], self.start[g, :Cn],
-                         self.members, n, self.Hkv) if Cn else -2
+        krow = np.ascontiguousarray(k_new[b]).reshape(-1)
+        # the candidates' rows before the update, kept so that a caller may replace
+        # the choice (adopt_layer_choice)
+        before = None
+        if len(cand):
+            st_, sz_, cp_ = self.start[g, cand], self.size[g, cand], self.cap[g, cand]
+            slots = np.where(sz_ < cp_, st_ + sz_, -1)
+            before = (self.cent[g, cand].copy(), sz_.copy(), slots,
+                      np.where(slots >= 0, self.members[np.maximum(slots, 0)], 0))
+        r = update_layer(krow, cand, self.cent[g, :Cn], self.size[g, :Cn], self.cap[g, :Cn],
+                         self.start[g, :Cn], self.members, n, self.Hkv) if Cn else -2
+        self._layer_undo[g] = (before, cand, krow, n)
         res[g] = (s, sel, k, cand, idx, outs, r)
 
     def _graph_step(self, g, q, k_new, budget, scale, M, max_len, res):

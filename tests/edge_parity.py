@@ -11,8 +11,10 @@ positive scale keep that bound, so scores may differ by at most
 Ranks are compared in order: a rank where the two lists hold different keys is
 accepted only if the oracle's score of the kernel's key lies within 2 tol_i of
 the oracle's score at that rank (a near-tie, where the kernel may legally choose
-the other key).  Everything else -- counts, padding, positions, pairs -- must match
-exactly.
+the other key).  Everything else -- counts, padding, positions -- must match
+exactly.  The co-attention pairs must equal the oracle's pairs
+(ckvo_coattention_pairs) of the oracle's own edge list, or, on a row where a
+near-tie changed the list, the oracle's pairs of the kernel's list.
 """
 from __future__ import annotations
 
@@ -77,24 +79,11 @@ def row_tolerance(Q: np.ndarray, K: np.ndarray, S: int, scale: float, rows) -> n
     return out
 
 
-def pairs_of(idx_row: np.ndarray, topk: int) -> np.ndarray:
-    """Co-attention pairs of one edge list: ascending positions, every pair, -1 padded."""
-    kept = sorted(int(j) for j in idx_row if j >= 0)
-    out = np.full((topk * (topk - 1) // 2, 2), -1, np.int32)
-    # pairs are enumerated over the topk slots, missing keys last
-    c = 0
-    for x in range(topk):
-        for y in range(x + 1, topk):
-            if y < len(kept):
-                out[c] = (kept[x], kept[y])
-            c += 1
-    return out
-
-
 def check_graph(idx_g, sc_g, pr_g, Q, K, S, scale, topk, rows, label=""):
     """Compare one graph's kernel rows with the oracle; returns the near-tie count."""
     rows = np.asarray(rows, np.int32)
     idx_o, sc_o = O.edges(Q, K, S, scale, topk, rows)
+    pr_o = O.coattention_pairs(idx_o, topk) if pr_g is not None else None
     tol = row_tolerance(Q, K, S, scale, rows)
     near = 0
     for r, i in enumerate(rows):
@@ -121,5 +110,8 @@ def check_graph(idx_g, sc_g, pr_g, Q, K, S, scale, topk, rows, label=""):
             assert (np.abs(zg - os_[diff].astype(np.float64)) <= 2 * t + 1e-30).all(), \
                 (where, "not a near-tie", gi, oi, zg, os_[diff], t)
         if pr_g is not None:
-            assert np.array_equal(pr_g[i], pairs_of(gi, topk)), (where, pr_g[i], gi)
+            # the oracle's pairs of the oracle's own list; where a near-tie put a
+            # different key in the kernel's list, the oracle's pairs of that list
+            want = pr_o[r] if not len(diff) else O.coattention_pairs(gi[None], topk)[0]
+            assert np.array_equal(pr_g[i], want), (where, pr_g[i], want)
     return near

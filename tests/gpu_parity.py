@@ -32,8 +32,39 @@ def _fail(msg):
     raise ParityError(msg)
 
 
-def compare_step(layer: Bd.DecodeLayer, res: dict, wl, t: int, out_stats: list):
-    """Compare one step's device outputs with the oracle's result dict."""
+# A layer graph's nearest candidate is decided on a squared distance over Hkv*d
+# elements.  The oracle sums it in fp64 in element order; the kernel sums each KV
+# head's slice apart and then the slices, so the two roundings differ by far less
+# than this bound (1024 terms: about 1e-13 relative).  A different choice is
+# accepted only between candidates this close; the oracle then takes the
+# kernel's choice, so one near-tie does not cascade over later steps.
+LAYER_TIE_REL = 1e-12
+
+
+def _layer_choice_excused(st, g: int, c_gpu: int, c_ora: int, log) -> bool:
+    cand, rows, krow = st.layer_candidate_rows(g)
+    ids = [int(c) for c in cand]
+    if rows is None or c_gpu not in ids or c_ora not in ids:
+        return False
+    k = krow.astype(np.uint32) << 16 if krow.dtype == np.uint16 else None
+    kl = (k.view(np.float32) if k is not None else krow).astype(np.longdouble)
+    dist = {c: float(((kl - rows[i].astype(np.longdouble)) ** 2).sum()) for i, c in enumerate(ids)}
+    dmin = min(dist.values())
+    if dist[c_gpu] - dmin > LAYER_TIE_REL * dmin:
+        return False
+    r = st.adopt_layer_choice(g, c_gpu)
+    if r != c_gpu:
+        return False
+    log(f"  excused layer-graph near-tie: graph {g} gpu={c_gpu} oracle={c_ora} "
+        f"(distances {dist[c_gpu]!r} / {dist[c_ora]!r}); the oracle takes the kernel's choice")
+    return True
+
+
+def compare_step(layer: Bd.DecodeLayer, res: dict, wl, t: int, out_stats: list, st=None,
+                 log=print):
+    """Compare one step's device outputs with the oracle's result dict.  With the
+    oracle state `st`, a layer graph's assignment may differ at a near-tie
+    (LAYER_TIE_REL), and the oracle then adopts the kernel's choice."""
     NG = layer.NG
     scores = layer.scores.cpu().numpy()
     sel = layer.selected.cpu().numpy()
@@ -63,6 +94,10 @@ def compare_step(layer: Bd.DecodeLayer, res: dict, wl, t: int, out_stats: list):
         if not np.array_equal(idx[g, :ilen[g]], res["idx"][g]):
             _fail(f"step {t} graph {g}: index lists differ")
         if assigned[g] != res["assigned"][g]:
+            if (layer.gpk == 0 and st is not None and assigned[g] >= 0 and res["assigned"][g] >= 0
+                    and _layer_choice_excused(st, g, int(assigned[g]), int(res["assigned"][g]),
+                                              log)):
+                continue
             _fail(f"step {t} graph {g}: assigned gpu={assigned[g]} oracle={res['assigned'][g]}")
     ref = res["out"]
     err = np.abs(out - ref)
@@ -132,7 +167,7 @@ def run_parity(wl, steps=None, li=0, index_stride=None, fused=False, log=print,
         t0 = time.perf_counter()
         res = st.step(qh, knh, vnh, wl.budget, wl.scale, wl.M, layer.index_list.shape[1])
         t_ora += time.perf_counter() - t0
-        compare_step(layer, res, wl, t, stats)
+        compare_step(layer, res, wl, t, stats, st=st, log=log)
         if steps > 4:
             log(f"  step {t + 1}/{steps} ok")
             sys.stdout.flush()

@@ -64,9 +64,24 @@ MUTANTS = {
                         "        for (int j = lo; j <= i; ++j) {"),
     "edge-scores-min-of-heads": ("best = dot > best ? dot : best;",
                                  "best = (h == 0 || dot < best) ? dot : best;"),
-    "layer-update-skips-last-slice": ("for (int sg = 0; sg < nseg; ++sg) {",
-                                      "for (int sg = 0; sg < nseg - 1; ++sg) {"),
-    "layer-update-slice-offset": ("long e = (long)sg * d + i;", "long e = i;"),
+    "layer-update-first-slice-only": (
+        "for (long e = 0; e < row; ++e) {\n            const double gap",
+        "for (long e = 0; e < d; ++e) {\n            const double gap"),
+    "layer-update-centroid-stride": (
+        "const double gap = widen(k_new, e, dtype) - (double)cent[(long)c * row + e];",
+        "const double gap = widen(k_new, e, dtype) - (double)cent[(long)c * d + e];"),
+    "pairs-higher-first": ("out[2 * slot] = y < cnt ? keys[x] : -1;\n"
+                           "                out[2 * slot + 1] = y < cnt ? keys[y] : -1;",
+                           "out[2 * slot] = y < cnt ? keys[y] : -1;\n"
+                           "                out[2 * slot + 1] = y < cnt ? keys[x] : -1;"),
+    "pairs-unsorted": ("while (at > 0 && keys[at - 1] > j) {",
+                       "while (at > 0 && keys[at - 1] > j && 0) {"),
+    "pairs-padding-on-lower-key": ("out[2 * slot] = y < cnt ? keys[x] : -1;\n"
+                                   "                out[2 * slot + 1] = y < cnt ? keys[y] : -1;",
+                                   "out[2 * slot] = x < cnt ? keys[x] : -1;\n"
+                                   "                out[2 * slot + 1] = x < cnt ? keys[y] : -1;"),
+    "pairs-skip-first-key": ("for (int t = 0; t < topk; ++t) {\n            int32_t j = idx",
+                             "for (int t = 1; t < topk; ++t) {\n            int32_t j = idx"),
     "edges-include-sinks": ("int lo = S;\n        int cnt", "int lo = 0;\n        int cnt"),
     "edges-tie-high-position": ("(arg < 0 || z[j] > z[arg])", "(arg < 0 || z[j] >= z[arg])"),
     "drift-not-relative": ("double r = den > 0.0 ? sqrt(num) / sqrt(den) : sqrt(num);",

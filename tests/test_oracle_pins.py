@@ -721,3 +721,92 @@ def test_layer_update_picks_the_nearest_whole_row():
         got = O.update_layer(kn, cand, cent, size, cap, start, members, 77, nseg)
         assert got == want, (trial, got, want)
         assert size[want] == 2 and members[start[want] + 1] == 77
+
+
+# ------------------------------------------ prefill token-graph co-attention pairs -----
+
+def test_coattention_pairs_worked_examples():
+    """The layout the C ABI documents for ckv_prefill_edges' pairs, on two rows of
+    topk = 3 and one of topk = 4: keys sorted ascending, slots (x, y) in
+    lexicographic order, a slot padded when its higher key is missing."""
+    p3 = O.coattention_pairs(np.array([[9, 5, -1], [7, 2, 4]], np.int32), 3)
+    assert p3[0].tolist() == [[5, 9], [-1, -1], [-1, -1]]
+    assert p3[1].tolist() == [[2, 4], [2, 7], [4, 7]]
+    p4 = O.coattention_pairs(np.array([[30, 10, 20, -1]], np.int32), 4)
+    assert p4[0].tolist() == [[10, 20], [10, 30], [-1, -1], [20, 30], [-1, -1], [-1, -1]]
+    # one key or none: no pair
+    assert (O.coattention_pairs(np.array([[6, -1, -1], [-1, -1, -1]], np.int32), 3) == -1).all()
+
+
+@pytest.mark.parametrize("topk", [2, 3, 5, 8])
+def test_coattention_pairs_are_every_two_subset_once(topk):
+    """Random rows with 0..topk distinct keys in any order: the valid pairs are
+    exactly the 2-subsets of the row's keys, each once, lower position first, in
+    ascending order; the padding count is what is left."""
+    r = rng(70 + topk)
+    rows = 200
+    idx = np.full((rows, topk), -1, np.int32)
+    for i in range(rows):
+        cnt = int(r.integers(0, topk + 1))
+        idx[i, :cnt] = r.choice(1000, cnt, replace=False)
+        r.shuffle(idx[i])
+    pr = O.coattention_pairs(idx, topk)
+    assert pr.shape == (rows, topk * (topk - 1) // 2, 2)
+    for i in range(rows):
+        keys = [int(j) for j in idx[i] if j >= 0]
+        valid = [tuple(p) for p in pr[i].tolist() if p != [-1, -1]]
+        assert all(a < b for a, b in valid), (i, valid)
+        assert set(valid) == set(itertools.combinations(sorted(keys), 2)), (i, keys, valid)
+        assert len(valid) == len(set(valid)) == len(keys) * (len(keys) - 1) // 2
+        assert valid == sorted(valid)
+        assert all(p == [-1, -1] or min(p) >= 0 for p in pr[i].tolist())
+
+
+def test_coattention_pairs_of_the_oracle_edges_link_keys_of_one_query():
+    """On a small prefill: every pair joins two keys that are both direct edges of
+    the same query, and a query with k keys has k(k-1)/2 pairs."""
+    r = rng(73)
+    n, d, G, S, topk = 30, 8, 2, 3, 4
+    Q = r.standard_normal((n, G, d)).astype(np.float32)
+    K = r.standard_normal((n, d)).astype(np.float32)
+    idx, _ = O.edges(Q, K, S, 0.5, topk)
+    pr = O.coattention_pairs(idx, topk)
+    for i in range(n):
+        keys = set(int(j) for j in idx[i] if j >= 0)
+        valid = [p for p in pr[i].tolist() if p != [-1, -1]]
+        assert all(a in keys and b in keys and a != b for a, b in valid)
+        k = min(topk, max(i - S, 0))
+        assert len(valid) == k * (k - 1) // 2
+
+
+def test_layer_state_adopts_another_candidate_exactly():
+    """Test plumbing for layer-graph near-ties: after a step, adopting candidate c
+    leaves the state exactly as an update with c as the only candidate from the
+    state before the step; adopting the oracle's own choice changes nothing."""
+    spec = I.granularity_spec(I.ConfigSpec("layer-adopt", 2, 8, 2, 16, 700, False, 64, 2,
+                                           I.DT_BF16), "layer")
+    wl = I.make_workload(spec, steps=2)
+    q, kn, vn = H.step_inputs(wl, 0, 0)
+    ref = H.oracle_state(wl)
+    pre = H.oracle_state(wl)
+    res = ref.step(q, kn, vn, wl.budget, wl.scale, wl.M, H.max_index_len(wl))
+    for g in range(wl.B):
+        own = int(res["assigned"][g])
+        cand = [int(c) for c in res["cand"][g] if c >= 0]
+        assert own in cand and len(cand) >= 2
+        other = next(c for c in cand if c != own)
+        # the oracle's own choice again: nothing changes
+        cent, size, mem = ref.cent.copy(), ref.size.copy(), ref.members.copy()
+        assert ref.adopt_layer_choice(g, own) == own
+        assert np.array_equal(ref.cent, cent) and np.array_equal(ref.size, size)
+        assert np.array_equal(ref.members, mem)
+        # another candidate: the single-candidate update on the pre-step state
+        assert ref.adopt_layer_choice(g, other) == other
+        Cn = int(pre.num_comms[g])
+        n = int(pre.seq_len[g])
+        krow = np.ascontiguousarray(kn[g]).reshape(-1)
+        assert O.update_layer(krow, np.array([other], np.int32), pre.cent[g, :Cn],
+                              pre.size[g, :Cn], pre.cap[g, :Cn], pre.start[g, :Cn],
+                              pre.members, n, wl.Hkv) == other
+        assert np.array_equal(ref.cent[g], pre.cent[g]) and np.array_equal(ref.size[g], pre.size[g])
+    assert np.array_equal(ref.members, pre.members)
