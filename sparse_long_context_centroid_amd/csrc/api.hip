@@ -38,9 +38,11 @@ ckv_status make_problem(const ckv_dims *d, Problem &p) {
     return CKV_OK;
 }
 
+// members may be null: an empty pool (no community has a member slot) has no
+// address, and no kernel reads or writes the pool of a community without slots
 ckv_status check_graphs(const ckv_graphs *g) {
     if (!g || !g->centroids || !g->num_comms || !g->comm_start || !g->comm_size ||
-        !g->comm_cap || !g->members)
+        !g->comm_cap)
         return CKV_ERR_INVALID_ARG;
     return CKV_OK;
 }

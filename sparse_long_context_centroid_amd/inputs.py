@@ -356,11 +356,6 @@ def _make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G, gpk, page_
         off += len(pool)
         assert off < 2**31
     members = np.concatenate(pools) if pools else np.zeros(0, np.int32)
-    if len(members) == 0:
-        # every token is a sink: no community has a member, but the pool still gets
-        # one free slot so that its device buffer has an address (the C ABI takes no
-        # null arrays)
-        members = np.full(1, -1, np.int32)
 
     # --- bulk keys / values on the device, written into the paged pool ----------
     k_pages = torch.zeros((num_pages, Hkv, PAGE_SIZE, d), dtype=tdt, device=device)

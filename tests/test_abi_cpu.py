@@ -72,7 +72,9 @@ def test_bad_dims_rejected(lib, kw, status):
 def test_null_pointers_and_small_workspace(lib):
     d = dims()
     fake = C.c_void_p(0x1000)
-    g = Bd.ckv_graphs(fake, fake, fake, fake, fake, None)           # members missing
+    g = Bd.ckv_graphs(None, fake, fake, fake, fake, fake)           # centroids missing
+    assert lib.ckv_score_centroids(C.byref(d), fake, C.byref(g), 0.1, fake, None) == -1
+    g = Bd.ckv_graphs(fake, fake, fake, None, fake, fake)           # sizes missing
     assert lib.ckv_score_centroids(C.byref(d), fake, C.byref(g), 0.1, fake, None) == -1
     g = Bd.ckv_graphs(fake, fake, fake, fake, fake, fake)
     assert lib.ckv_score_centroids(C.byref(d), None, C.byref(g), 0.1, fake, None) == -1
@@ -99,6 +101,23 @@ def test_null_pointers_and_small_workspace(lib):
     assert lib.ckv_decode_step(C.byref(d), fake, fake, fake, C.byref(g), C.byref(kv), fake, 0,
                                0.1, fake, fake, 2052, fake, None, fake, None, fake, fake, fake,
                                1 << 30, fake, None, None) == -1
+
+
+def test_empty_member_pool_passes_validation(lib):
+    """A null member pool (no community has a slot) is a valid graph set: the calls
+    that take graphs reach the next check -- here a workspace that is too small, or
+    a candidate count out of range -- instead of rejecting the pool."""
+    d = dims()
+    fake = C.c_void_p(0x1000)
+    g = Bd.ckv_graphs(fake, fake, fake, fake, fake, None)
+    kv = Bd.ckv_kv(fake, fake, fake, 16, 8, 8, fake)
+    assert lib.ckv_decode_step(C.byref(d), fake, fake, fake, C.byref(g), C.byref(kv), fake, 8,
+                               0.1, fake, fake, 2052, fake, None, fake, None, fake, fake, fake,
+                               64, fake, None, None) == -3
+    assert lib.ckv_select(C.byref(d), fake, C.byref(g), fake, fake, 0, fake, 2052, fake, None,
+                          fake, None, fake, None) == -1
+    assert lib.ckv_local_update(C.byref(d), fake, fake, fake, 0, C.byref(g), C.byref(kv), fake,
+                                fake, None) == -1
 
 
 def test_dense_entry_points_validate(lib):

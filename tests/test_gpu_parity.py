@@ -261,6 +261,19 @@ def test_parity_contexts_shorter_than_sinks(fused):
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["four-calls", "fused-step"])
+def test_parity_all_sinks_null_member_pool(fused):
+    """Every sequence holds sinks only: no community exists, the member pool is
+    empty and reaches the library as a null pointer; the lists are the sinks and
+    the new token is still appended."""
+    _case("all sinks, null member pool")
+    wl = I.make_workload(1, device="cuda", contexts=[3, 4, 2], steps=2)
+    assert wl.layers[0].members.size == 0
+    layer = Bd.decode_layer_from_workload(wl, 0)
+    assert layer.graphs.members is None
+    run_parity(wl, fused=fused)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["four-calls", "fused-step"])
 def test_parity_empty_communities(fused):
     """Communities of size 0 (members never listed) score -inf and are never kept
     or candidates."""
