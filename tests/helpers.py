@@ -18,22 +18,24 @@ def raw_np(t: torch.Tensor) -> np.ndarray:
 
 
 def logical_kv(wl, layer):
-    """[B, Hkv, max_pages*PAGE, d] raw K and V in token order, through the page table."""
-    pt = wl.page_table.cpu().numpy()
-    kp = raw_np(layer.k_pages)
-    vp = raw_np(layer.v_pages)
+    """[B, Hkv, max_pages*PAGE, d] raw K and V in token order, through the page table
+    (a gather of whole pages where the pages live, then one copy to the host;
+    unmapped pages read as zeros)."""
+    pt = wl.page_table
+    kp, vp = layer.k_pages, layer.v_pages
+    pt = pt.to(kp.device).long()
     B, P = pt.shape
     ps = wl.page_size
-    K = np.zeros((B, wl.Hkv, P * ps, wl.d), kp.dtype)
-    V = np.zeros_like(K)
-    for b in range(B):
-        for p in range(P):
-            pg = pt[b, p]
-            if pg < 0:
-                continue
-            K[b, :, p * ps:(p + 1) * ps] = kp[pg]
-            V[b, :, p * ps:(p + 1) * ps] = vp[pg]
-    return K, V
+    mapped = (pt >= 0)
+    sel = pt.clamp(min=0).reshape(-1)
+
+    def gather(pool):
+        g = pool.index_select(0, sel).reshape(B, P, wl.Hkv, ps, wl.d)
+        if not bool(mapped.all()):
+            g = torch.where(mapped.reshape(B, P, 1, 1, 1), g, torch.zeros_like(g))
+        return raw_np(g.permute(0, 2, 1, 3, 4).reshape(B, wl.Hkv, P * ps, wl.d))
+
+    return gather(kp), gather(vp)
 
 
 def oracle_state(wl, li=0, threads=None) -> O.OracleState:

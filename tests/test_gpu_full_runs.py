@@ -1,0 +1,119 @@
+"""GPU parity at the workloads' own run lengths, and determinism of the fused step.
+
+* 1 x 32K group graphs and 1 x 32K per-head graphs: 64 decode steps each;
+  4 x 128K: 256 decode steps -- every step compared with the oracle (scores, sets,
+  candidates, lists, assignments, attention), then the whole state (centroids bit
+  for bit after every local update, sizes, member pools, the appended K/V rows).
+  Over a long generation the local assignments drift (rit.work post "CommunityKV
+  long-context decoding", section "Когда CommunityKV стоит включить в план
+  инфраструктуры"): the fp32 running means must stay identical on both sides
+  through all of it.
+* the 16-sequence ragged, paged workload with all 36 layers: every layer's fused
+  step against the oracle, layers 0, 17 and 35 for two steps.
+* determinism: the same fused step run twice from the same state gives identical
+  bytes in every output and in the updated state.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_parity import run_parity
+from sparse_long_context_centroid_amd import binding as Bd
+from sparse_long_context_centroid_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    Bd.load()
+
+
+def _case(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def _every(k):
+    def log(m):
+        if "parity ok" in m or "ready" in m:
+            print(m, flush=True)
+        elif m.strip().startswith("step ") and int(m.split()[1].split("/")[0]) % k == 0:
+            print(m, flush=True)
+    return log
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_full_run_length(cfg):
+    spec = I.CONFIGS[cfg]
+    _case(f"{spec.name}: all {spec.steps} decode steps, fused step")
+    wl = I.make_workload(cfg, device="cuda")
+    assert wl.steps == spec.steps
+    s = run_parity(wl, fused=True, log=_every(16))
+    assert s["steps"] == spec.steps
+
+
+@pytest.fixture(scope="module")
+def ragged36():
+    spec = I.CONFIGS[4]
+    print(f"\n[case] {spec.name}: generating all {spec.layers} layers", flush=True)
+    wl = I.make_workload(4, device="cuda", steps=2)
+    assert len(wl.layers) == spec.layers == 36
+    yield wl
+    del wl
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("li", list(range(36)))
+def test_ragged_paged_every_layer(ragged36, li):
+    """One layer of the 16-sequence ragged, paged 36-layer workload (each layer has
+    its own K/V pool, partitions and centroids; the page table is shared): its
+    fused step against the oracle, two steps for layers 0, 17 and 35."""
+    steps = 2 if li in (0, 17, 35) else 1
+    _case(f"{ragged36.spec.name} layer {li}: {steps} step(s)")
+    run_parity(ragged36, steps=steps, li=li, fused=True, log=_every(1 << 30))
+
+
+def _snapshot(layer: Bd.DecodeLayer):
+    torch.cuda.synchronize()
+    t = {k: getattr(layer, k).detach().cpu().clone() for k in
+         ("scores", "selected", "num_selected", "cand", "index_len", "index_list", "assigned",
+          "out", "centroids", "comm_size", "members", "seq_len", "err")}
+    return t
+
+
+@pytest.mark.parametrize("cfg,kw", [
+    (3, dict(steps=2)),
+    (2, dict(steps=2)),
+    (I.granularity_spec(I.CONFIGS[1], "layer"), dict(steps=2, context=8192)),
+    (4, dict(steps=2, layers=1)),
+])
+def test_fused_step_is_deterministic(cfg, kw):
+    """Two device layers built from the same state take the same two steps: every
+    output and every state array must be bit-identical between the runs."""
+    _case(f"determinism {getattr(cfg, 'name', cfg)} {kw}")
+    wl = I.make_workload(cfg, device="cuda", **kw)
+    L = wl.layers[0]
+    snaps = []
+    for run in range(2):
+        # K/V pools are shared: a step appends row n with the same bytes each run,
+        # and attention reads only rows below n
+        layer = Bd.decode_layer_from_workload(wl, 0)
+        per_step = []
+        for t in range(2):
+            layer.step_fused(L.q[t].contiguous(), L.k_new[t].contiguous(),
+                             L.v_new[t].contiguous(), wl.scale)
+            per_step.append(_snapshot(layer))
+        assert int(layer.err.item()) == 0
+        snaps.append(per_step)
+        del layer
+    for t in range(2):
+        a, b = snaps[0][t], snaps[1][t]
+        for k in a:
+            x, y = a[k], b[k]
+            if x.dtype == torch.float32:
+                x, y = x.view(torch.int32), y.view(torch.int32)
+            assert torch.equal(x, y), f"step {t}: {k} differs between two runs"

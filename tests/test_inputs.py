@@ -36,3 +36,25 @@ def test_layers_share_stride_and_members_are_own_positions(cfg, kw):
             spans += [(int(s), int(s + c)) for s, c in zip(st, cap)]
         spans.sort()
         assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+
+
+def test_logical_kv_gather_matches_the_page_walk():
+    """The test-side gather of the paged pools into token order equals a plain walk
+    over the page table (unmapped pages stay zero)."""
+    import helpers as H
+    wl = I.make_workload(4, contexts=[700, 1600, 33], steps=2, layers=1)
+    L = wl.layers[0]
+    K, V = H.logical_kv(wl, L)
+    pt = wl.page_table.cpu().numpy()
+    kp, vp = H.raw_np(L.k_pages), H.raw_np(L.v_pages)
+    B, P = pt.shape
+    ps = wl.page_size
+    K2 = np.zeros((B, wl.Hkv, P * ps, wl.d), kp.dtype)
+    V2 = np.zeros_like(K2)
+    for b in range(B):
+        for p in range(P):
+            if pt[b, p] >= 0:
+                K2[b, :, p * ps:(p + 1) * ps] = kp[pt[b, p]]
+                V2[b, :, p * ps:(p + 1) * ps] = vp[pt[b, p]]
+    assert (pt < 0).any()
+    assert np.array_equal(K, K2) and np.array_equal(V, V2)
