@@ -81,19 +81,25 @@ def step_bytes(layer: Bd.DecodeLayer, idx_len: np.ndarray, elem: int):
 
 KERNELS = ["score", "select", "attn_update", "merge"]
 
-PMC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_b4_ctx128k_pmc_traffic.txt")
+# rocprofv3 FETCH_SIZE / WRITE_SIZE summaries of the attention launch, per workload
+PMC_FILES = {
+    "qwen3-8b-layer-b4-ctx128k-group": "attn_kernel_b4_ctx128k_pmc_traffic.txt",
+    "qwen3-8b-36layer-ragged16-ctx8k-128k-paged": "attn_kernel_ragged16_36layer_pmc_traffic.txt",
+}
 ATTN_SOURCES = ["attn.hip", "update_rule.h", "ckv_device.h", "ckv_internal.h"]
 
 
 def measured_traffic(workload: str):
     """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary (calibrated against a plain copy), or None when the
-    summary is for another workload or the attention kernel's sources changed
-    since the counters were taken."""
+    WRITE_SIZE summary (calibrated against a plain copy), or None when there is no
+    summary for this workload or the attention kernel's sources changed since the
+    counters were taken."""
     import hashlib
-    if workload != "qwen3-8b-layer-b4-ctx128k-group" or not os.path.exists(PMC_FILE):
+    name = PMC_FILES.get(workload)
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if path is None or not os.path.exists(path):
         return None
-    txt = open(PMC_FILE).read()
+    txt = open(path).read()
     h = hashlib.sha256()
     for f in ATTN_SOURCES:
         h.update(open(os.path.join(ROOT, "sparse_long_context_centroid_amd", "csrc", f), "rb").read())
@@ -133,7 +139,7 @@ def dense_baseline(layers, qkv, wl, scrub, args, elem):
     token, no selection), same cold protocol, on the state the sparse steps left."""
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     outs = [torch.empty_like(l.out) for l in layers]
-    T = args.warmup + args.steps
+    T = qkv[0][0].shape[0]
     ms = []
     for t in range(min(args.steps, 10) + 2):
         tot = 0.0
@@ -313,13 +319,37 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def oracle_threads() -> tuple:
+    """Threads for the oracle: every CPU this process may run on, capped by the
+    host's declared CPU share for this job (OMP_NUM_THREADS when it is set)."""
+    aff = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return (min(aff, int(cap)) if cap.isdigit() and int(cap) > 0 else aff), aff
+
+
 def cpu_baseline(wl, seconds: float, threads: int):
-    """The fp64 oracle on the host cores, on the first steps of layer 0."""
+    """The fp64 oracle on the host cores.  One-layer workloads: the first decode
+    steps of the layer, as many as fit in `seconds`.  Multi-layer workloads: one
+    whole decode step, the layers streamed one at a time (each layer's host copy
+    is made outside the timed region), the per-layer times summed."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import helpers as H  # test infrastructure: host copies for the oracle
-    st = H.oracle_state(wl, 0, threads=threads)
-    L = wl.layers[0]
     max_len = int(wl.S + wl.budget.max())
+    layers = len(wl.layers)
+    if layers > 1:
+        total = 0.0
+        for li in range(layers):
+            st = H.oracle_state(wl, li, threads=threads)
+            q, kn, vn = H.step_inputs(wl, li, 0)
+            t0 = time.perf_counter()
+            st.step(q, kn, vn, wl.budget, wl.scale, wl.M, max_len)
+            total += time.perf_counter() - t0
+            del st
+        return dict(value=wl.B / total, unit="tokens/s", cores=threads, kind="oracle",
+                    sample=f"one decode step of all {layers} layers x {wl.B} sequences, layers "
+                           f"streamed one at a time (host copies untimed), fp64 C oracle, "
+                           f"{threads} threads over graphs", seconds=total)
+    st = H.oracle_state(wl, 0, threads=threads)
     done = 0
     t0 = time.perf_counter()
     while done < wl.steps:
@@ -329,11 +359,192 @@ def cpu_baseline(wl, seconds: float, threads: int):
         if time.perf_counter() - t0 > seconds:
             break
     dt = time.perf_counter() - t0
-    layers = len(wl.layers)
-    return dict(value=wl.B * done / dt / layers, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{done} decode steps x {wl.B} sequences of layer 0 "
-                       f"({'scaled by 1/%d layers' % layers if layers > 1 else 'the whole step'})"
-                       f", fp64 C oracle, {threads} threads over graphs")
+    return dict(value=wl.B * done / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{done} decode steps x {wl.B} sequences of the layer (the whole step), "
+                       f"fp64 C oracle, {threads} threads over graphs", seconds=dt)
+
+
+def update_cost_vs_context(args, scrub, contexts=(8192, 131072), steps=24):
+    """The local update alone (ckv_local_update, one launch) on the 4-sequence
+    Qwen3-8B layer shape at two context lengths: its cost is set by the candidate
+    count and d, not by n.  Each timed call follows a cold-cache scrub; HIP events
+    bracket the single launch on its stream.  The candidates come from the same
+    step's score and selection (untimed)."""
+    out = {}
+    for n in contexts:
+        wl = I.make_workload(3, args.seed, device="cuda:0", context=n, steps=steps, layers=1)
+        lay = build_layers(wl, int(wl.S + wl.budget.max()))[0]
+        L = wl.layers[0]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        us = []
+        for t in range(steps):
+            lay.score(L.q[t], wl.scale)
+            lay.select()
+            if not args.warm:
+                scrub_sum = scrub.sum()
+            ev[0].record()
+            lay.update(L.k_new[t], L.v_new[t])
+            ev[1].record()
+            torch.cuda.synchronize()
+            if t >= 4:
+                us.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        if int(lay.err.item()):
+            raise SystemExit("device error flag during the update timing")
+        out[str(n)] = dict(us_median=float(np.median(us)), us_mean=float(np.mean(us)),
+                           graphs=lay.NG, communities_per_graph=float(L.num_comms.mean()),
+                           calls=len(us))
+        del lay, wl, L
+        torch.cuda.empty_cache()
+    a, b = (out[str(c)]["us_median"] for c in contexts)
+    out["ratio_long_over_short"] = b / a
+    out["what"] = ("ckv_local_update alone (candidates from the same step), 4 sequences x 8 KV "
+                   "heads, M = 8, d = 128; event pair around the launch after a cache scrub")
+    return out
+
+
+def measure(spec, args, scrub, *, extras: bool):
+    """Generate `spec` on the GPU and time its fused decode step.  Passes, in order:
+    warmup; K steps bracketed by a pair of events each (value); K steps with the
+    per-kernel events (kernel times, roofline); without --warm, up to 20
+    back-to-back steps without the scrub; then the configuration's remaining
+    decode steps, untimed, so that every step the configuration runs is run.
+    With `extras`: centroid rebuild, the dense baseline, the granularity sweep and
+    the prefill edges as well."""
+    dev = "cuda:0"
+    KW = 0 if args.warm else min(args.steps, 20)
+    T_timed = args.warmup + 2 * args.steps + KW
+    T = max(T_timed, spec.steps)
+    t0 = time.perf_counter()
+    wl = I.make_workload(spec, args.seed, device=dev, steps=T,
+                         layers=args.layers if extras else None)
+    torch.cuda.synchronize()
+    log(f"[bench] workload {spec.name}: {len(wl.layers)} layer(s), B={wl.B}, "
+        f"n={wl.seq_len0.tolist()[:4]}..., Cmax={wl.Cmax}, {T} steps, generated in "
+        f"{time.perf_counter() - t0:.1f}s")
+    index_stride = int(wl.S + wl.budget.max())
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads, aff = oracle_threads()
+        t1 = time.perf_counter()
+        cpu = cpu_baseline(wl, args.cpu_seconds, threads)
+        cpu["affinity_cpus"] = aff
+        cpu["threads_rule"] = "min(len(sched_getaffinity), OMP_NUM_THREADS when set)"
+        if len(wl.layers) == 1:
+            one = cpu_baseline(wl, max(2.0, args.cpu_seconds / 5), 1)
+            cpu["value_1_thread"] = one["value"]
+            cpu["sample_1_thread"] = one["sample"]
+        cpu["cpu_model"] = cpu_model()
+        log(f"[bench] cpu baseline {cpu['value']:.2f} tokens/s on {threads} threads "
+            f"({time.perf_counter() - t1:.1f}s)")
+    layers = build_layers(wl, index_stride)
+    timers = [Timed(l) for l in layers]
+    elem = 2 if wl.dtype == I.DT_BF16 else 4
+    qkv = [(L.q, L.k_new, L.v_new) for L in wl.layers]
+    kernel_ms = np.zeros(4)
+    kernel_bytes = {k: 0 for k in KERNELS}
+    attn_only_bytes = 0
+    step_ms, step_ms_instr, step_ms_warm = [], [], []
+    value_bytes = 0
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for t in range(T):
+        phase = 0 if t < args.warmup else (1 if t < args.warmup + args.steps else (
+            2 if t < args.warmup + 2 * args.steps else (3 if t < T_timed else 4)))
+        tot = 0.0
+        for li, (tm, (q, kn, vn)) in enumerate(zip(timers, qkv)):
+            if not args.warm and phase in (1, 2):
+                scrub_sum = scrub.sum()               # cold caches, outside the events
+            tm.run(q[t], kn[t], vn[t], wl.scale, per_kernel=phase == 2)
+            if phase == 4:
+                continue
+            torch.cuda.synchronize()
+            if phase == 3:
+                tot += tm.step_ms()
+            elif phase:
+                tot += tm.step_ms()
+                idx_len = tm.layer.index_len.cpu().numpy()
+                by, ab = step_bytes(tm.layer, idx_len, elem)
+                if phase == 1:
+                    value_bytes += sum(by.values())
+                else:
+                    kernel_ms += np.array(tm.times_ms())
+                    for k, v in by.items():
+                        kernel_bytes[k] += v
+                    attn_only_bytes += ab
+        if phase == 1:
+            step_ms.append(tot)
+        elif phase == 2:
+            step_ms_instr.append(tot)
+        elif phase == 3:
+            step_ms_warm.append(tot)
+        if t == 0 or (t + 1) % 25 == 0:
+            log(f"[bench] step {t + 1}/{T}")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    err = max(int(l.err.item()) for l in layers)
+    if err:
+        raise SystemExit(f"device error flag {err} during the benchmark")
+    K = args.steps
+    nl = len(layers)
+    total_ms = float(np.sum(step_ms))
+    per_kernel = {n: dict(ms_per_launch=kernel_ms[i] / (K * nl),
+                          gbs=kernel_bytes[n] / (kernel_ms[i] / 1e3) / 1e9 if kernel_ms[i] else None)
+                  for i, n in enumerate(KERNELS)}
+    attn_gbs = per_kernel["attn_update"]["gbs"]
+    path_gbs = value_bytes / (total_ms / 1e3) / 1e9
+    r = {
+        "workload": spec.name,
+        "value": wl.B * K / (total_ms / 1e3),
+        "ms_per_step": total_ms / K,
+        "ms_per_step_median": float(np.median(step_ms)),
+        "config": {
+            "workload": spec.name, "batch": wl.B, "layers": nl,
+            "context": int(wl.seq_len0.max()) if not spec.ragged else "8K-128K ragged",
+            "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d,
+            "graphs": "per-head" if wl.gpk > 1 else ("per-layer" if wl.gpk == 0 else "query-group"),
+            "budget": int(wl.budget.max()) if not spec.ragged else "5% of context",
+            "sinks": wl.S, "n_cand": wl.M, "kv_dtype": "bf16" if elem == 2 else "fp32",
+            "score_arith": "fp64", "attn_arith": "fp32", "steps_run": T,
+            "protocol": "warm (back-to-back)" if args.warm else
+            f"cold ({args.scrub_mib} MiB scrub before each layer's step, outside the events)",
+        },
+        "dtype": "bf16" if elem == 2 else "fp32",
+        "path_gbs": path_gbs,
+        "path_frac_hbm": path_gbs / HBM_PEAK_GBS,
+        "path_frac_target": 0.60,
+        "path_target_met": path_gbs / HBM_PEAK_GBS >= 0.60,
+        "bytes_per_step": value_bytes / K,
+        "ms_per_step_with_kernel_events": float(np.mean(step_ms_instr)),
+        "warm": ({"ms_per_step": float(np.mean(step_ms_warm)),
+                  "tokens_per_s": wl.B / (float(np.mean(step_ms_warm)) / 1e3),
+                  "steps": len(step_ms_warm),
+                  "protocol": "back-to-back steps, no scrub; the host synchronises and reads "
+                              "results after every step, so its launch latency is exposed"}
+                 if step_ms_warm else None),
+        "kernels": per_kernel,
+        "attn_share_of_attn_update_bytes": attn_only_bytes / kernel_bytes["attn_update"],
+        "wall_s_timed_loop": wall,
+        "roofline": {
+            "kernel": "attn_kernel (indexed split-K flash-decode partials + local update)",
+            "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": attn_gbs / HBM_PEAK_GBS if attn_gbs else None,
+            "traffic": measured_traffic(spec.name),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes_per_launch": kernel_bytes["attn_update"] / (K * nl),
+        },
+        "cpu_baseline": cpu,
+    }
+    if extras and not args.no_rebuild:
+        r["centroid_rebuild"] = rebuild_timing(layers, scrub, args, elem)
+    if not args.no_dense:
+        dense = dense_baseline(layers, qkv, wl, scrub, args, elem)
+        dense["sparse_speedup"] = dense["ms_per_step"] / (total_ms / K)
+        r["dense_baseline"] = dense
+    if extras and not args.no_edges:
+        r["prefill_edges"] = edges_timing(wl, args)
+    del layers, timers, qkv, wl
+    torch.cuda.empty_cache()
+    return r
 
 
 def main():
@@ -357,6 +568,10 @@ def main():
                     help="skip the graph-granularity sweep (group / per-head / per-layer)")
     ap.add_argument("--no-edges", action="store_true",
                     help="skip the prefill edge-extraction measurement")
+    ap.add_argument("--no-update-timing", action="store_true",
+                    help="skip timing the local update alone at 8K and 128K contexts")
+    ap.add_argument("--no-config4", action="store_true",
+                    help="skip the 36-layer ragged paged workload measured after the main one")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before timing, run a plain device copy of this many MiB three times "
@@ -370,35 +585,9 @@ def main():
     Bd.load()
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    # warmup, then K steps timed as a whole (value), then K steps with per-kernel
-    # events (roofline); the per-kernel events are kept out of the value pass
-    # ... then (cold protocol only) a few back-to-back steps without the scrub
-    KW = 0 if args.warm else min(args.steps, 20)
-    T = args.warmup + 2 * args.steps + KW
     spec = I.CONFIGS[args.config]
     if args.graphs != "config":
         spec = I.granularity_spec(spec, args.graphs)
-    t0 = time.perf_counter()
-    wl = I.make_workload(spec, args.seed, device=dev, steps=T, layers=args.layers)
-    torch.cuda.synchronize()
-    log(f"[bench] workload {spec.name}: {len(wl.layers)} layer(s), B={wl.B}, "
-        f"n={wl.seq_len0.tolist()[:4]}..., Cmax={wl.Cmax}, generated in "
-        f"{time.perf_counter() - t0:.1f}s")
-    index_stride = int(wl.S + wl.budget.max())
-    cpu = None
-    if not args.no_cpu_baseline:
-        threads = min(len(os.sched_getaffinity(0)), 16)
-        t1 = time.perf_counter()
-        cpu = cpu_baseline(wl, args.cpu_seconds, threads)
-        one = cpu_baseline(wl, max(2.0, args.cpu_seconds / 5), 1)
-        cpu["value_1_thread"] = one["value"]
-        cpu["sample_1_thread"] = one["sample"]
-        cpu["cpu_model"] = cpu_model()
-        log(f"[bench] cpu baseline {cpu['value']:.1f} tokens/s, 1 thread {one['value']:.1f} "
-            f"({time.perf_counter() - t1:.1f}s)")
-    layers = build_layers(wl, index_stride)
-    timers = [Timed(l) for l in layers]
-    elem = 2 if wl.dtype == I.DT_BF16 else 4
     scrub = torch.empty(args.scrub_mib << 18, dtype=torch.float32, device=dev).fill_(0.0)
     if args.copy_mib:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
@@ -407,125 +596,37 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    qkv = [(L.q, L.k_new, L.v_new) for L in wl.layers]
-    kernel_ms = np.zeros(4)
-    kernel_bytes = {k: 0 for k in KERNELS}
-    attn_only_bytes = 0
-    step_ms, step_ms_instr, step_ms_warm = [], [], []
-    value_bytes = 0
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for t in range(T):
-        phase = 0 if t < args.warmup else (1 if t < args.warmup + args.steps else (
-            2 if t < args.warmup + 2 * args.steps else 3))
-        tot = 0.0
-        for li, (tm, (q, kn, vn)) in enumerate(zip(timers, qkv)):
-            if not args.warm and phase != 3:
-                scrub_sum = scrub.sum()               # cold caches, outside the events
-            tm.run(q[t], kn[t], vn[t], wl.scale, per_kernel=phase == 2)
-            torch.cuda.synchronize()
-            if phase == 3:
-                tot += tm.step_ms()
-            elif phase:
-                tot += tm.step_ms()
-                idx_len = tm.layer.index_len.cpu().numpy()
-                by, ab = step_bytes(tm.layer, idx_len, elem)
-                if phase == 1:
-                    value_bytes += sum(by.values())
-                else:
-                    kernel_ms += np.array(tm.times_ms())
-                    for k, v in by.items():
-                        kernel_bytes[k] += v
-                    attn_only_bytes += ab
-        if phase == 1:
-            step_ms.append(tot)
-        elif phase == 2:
-            step_ms_instr.append(tot)
-        elif phase == 3:
-            step_ms_warm.append(tot)
-        if t == 0 or (t + 1) % 10 == 0:
-            log(f"[bench] step {t + 1}/{T}")
-    wall = time.perf_counter() - wall0
-    rebuild = None
-    if not args.no_rebuild:
-        rebuild = rebuild_timing(layers, scrub, args, elem)
-    dense = None
-    if not args.no_dense:
-        dense = dense_baseline(layers, qkv, wl, scrub, args, elem)
-    sweep = None
-    if not args.no_granularity:
-        sweep = granularity_sweep(spec, args, scrub, elem)
-    edges = None
-    if not args.no_edges:
-        edges = edges_timing(wl, args)
-    err = max(int(l.err.item()) for l in layers)
-    if err:
-        raise SystemExit(f"device error flag {err} during the benchmark")
-
-    K = args.steps
-    total_ms = float(np.sum(step_ms))
-    toks = wl.B * K
-    value = toks / (total_ms / 1e3)
-    all_bytes = value_bytes
-    names = KERNELS
-    per_kernel = {n: dict(ms_per_launch=kernel_ms[i] / (K * len(layers)),
-                          gbs=kernel_bytes[n] / (kernel_ms[i] / 1e3) / 1e9 if kernel_ms[i] else None)
-                  for i, n in enumerate(names)}
-    attn_gbs = per_kernel["attn_update"]["gbs"]
+    main_r = measure(spec, args, scrub, extras=True)
     res = {
         "metric": "sparse decode attention tokens/s + achieved HBM GB/s at 128K, Qwen3-8B shape",
-        "value": value,
+        "value": main_r["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": total_ms / K,
-        "ms_per_step_median": float(np.median(step_ms)),
+        "ms_per_step": main_r["ms_per_step"],
+        "ms_per_step_median": main_r["ms_per_step_median"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": main_r["dtype"],
         "data": "synthetic",
-        "config": {
-            "workload": spec.name, "batch": wl.B, "layers": len(wl.layers),
-            "context": int(wl.seq_len0.max()) if not spec.ragged else "8K-128K ragged",
-            "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d,
-            "graphs": "per-head" if wl.gpk > 1 else ("per-layer" if wl.gpk == 0 else "query-group"),
-            "budget": int(wl.budget.max()) if not spec.ragged else "5% of context",
-            "sinks": wl.S, "n_cand": wl.M, "kv_dtype": "bf16" if elem == 2 else "fp32",
-            "score_arith": "fp64", "attn_arith": "fp32", "protocol": "warm (back-to-back)" if args.warm else
-            f"cold ({args.scrub_mib} MiB scrub between steps)",
-        },
-        "path_gbs": all_bytes / (total_ms / 1e3) / 1e9,
-        "path_frac_hbm": all_bytes / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-        "bytes_per_step": all_bytes / K,
-        "ms_per_step_with_kernel_events": float(np.mean(step_ms_instr)),
-        "warm": ({"ms_per_step": float(np.mean(step_ms_warm)),
-                  "tokens_per_s": wl.B / (float(np.mean(step_ms_warm)) / 1e3),
-                  "steps": len(step_ms_warm),
-                  "protocol": "back-to-back steps, no scrub"} if step_ms_warm else None),
-        "kernels": per_kernel,
-        "attn_share_of_attn_update_bytes": attn_only_bytes / kernel_bytes["attn_update"],
-        "wall_s_timed_loop": wall,
-        "roofline": {
-            "kernel": "attn_kernel (indexed split-K flash-decode partials + local update)",
-            "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": attn_gbs / HBM_PEAK_GBS if attn_gbs else None,
-            "traffic": measured_traffic(spec.name),
-            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "algorithmic_bytes_per_launch": kernel_bytes["attn_update"] / (K * len(layers)),
-        },
-        "cpu_baseline": cpu,
     }
-    if rebuild is not None:
-        res["centroid_rebuild"] = rebuild
-    if dense is not None:
-        dense["sparse_speedup"] = dense["ms_per_step"] / (total_ms / K)
-        res["dense_baseline"] = dense
-    if sweep is not None:
-        res["granularity_sweep"] = sweep
-    if edges is not None:
-        res["prefill_edges"] = edges
+    for k, v in main_r.items():
+        if k not in res and k not in ("workload",):
+            res[k] = v
+    if not args.no_update_timing:
+        res["update_cost_vs_context"] = update_cost_vs_context(args, scrub)
+        u = res["update_cost_vs_context"]
+        log(f"[bench] local update alone: {u['8192']['us_median']:.2f} us at 8K, "
+            f"{u['131072']['us_median']:.2f} us at 128K")
+    if not args.no_granularity:
+        res["granularity_sweep"] = granularity_sweep(spec, args, scrub, 2 if spec.dtype == I.DT_BF16 else 4)
+    if args.config != 4 and not args.no_config4:
+        c4 = measure(I.CONFIGS[4], args, scrub, extras=False)
+        res["config4"] = {k: v for k, v in c4.items() if k not in ("dtype",)}
+        log(f"[bench] {c4['workload']}: {c4['ms_per_step']:.3f} ms per 36-layer step, "
+            f"{c4['value']:.0f} tokens/s, path {c4['path_frac_hbm']:.3f} of HBM peak")
     print(json.dumps(res), flush=True)
 
 
