@@ -328,6 +328,32 @@ CKV_API ckv_status ckv_decode_step(const ckv_dims *dims, const void *q, const vo
                                    size_t ws_bytes, int32_t *err_flag, void *const *events,
                                    void *stream);
 
+/*
+ * ckv_decode_step for callers that cannot allocate device memory (code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step and results, with the scratch in an array the library
+ * holds in device memory (one per GPU it runs on, kept until the process ends)
+ * instead of a caller's workspace.  No call allocates or frees memory.
+ *   - a step whose ckv_workspace_size(dims, index_stride) exceeds
+ *     CKV_NOALLOC_SCRATCH_BYTES returns CKV_ERR_WORKSPACE before anything is
+ *     enqueued;
+ *   - the array holds no state a step relies on (every step writes the scratch it
+ *     reads); calls that overlap on one GPU (several streams or threads at once)
+ *     share it and race: serialise them;
+ *   - CKV_ERR_HIP when the array's device address cannot be obtained.
+ * Other arguments and the events are those of ckv_decode_step.
+ */
+#define CKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+CKV_API ckv_status ckv_decode_step_noalloc(const ckv_dims *dims, const void *q,
+                                           const void *k_new, const void *v_new,
+                                           const ckv_graphs *graphs, const ckv_kv *kv,
+                                           const int32_t *budget, int32_t n_cand, float scale,
+                                           float *scores, int32_t *index_list,
+                                           int32_t index_stride, int32_t *index_len,
+                                           int32_t *num_selected, int32_t *cand,
+                                           uint8_t *selected, int32_t *assigned, float *out,
+                                           int32_t *err_flag, void *const *events, void *stream);
+
 CKV_API const char *ckv_status_string(ckv_status status);
 
 #ifdef __cplusplus

@@ -69,6 +69,8 @@ def load(path: str = LIB_PATH):
         "ckv_local_update": (i32, [pd, P, P, P, i32, pg, pk, P, P, P]),
         "ckv_decode_step": (i32, [pd, P, P, P, pg, pk, P, i32, C.c_float, P, P, i32, P, P, P,
                                   P, P, P, P, sz, P, P, P]),
+        "ckv_decode_step_noalloc": (i32, [pd, P, P, P, pg, pk, P, i32, C.c_float, P, P, i32, P,
+                                          P, P, P, P, P, P, P, P]),
         "ckv_dense_workspace_size": (sz, [pd, pk]),
         "ckv_dense_decode_attn": (i32, [pd, P, pk, C.c_float, P, P, sz, P, P]),
         "ckv_rebuild_centroids": (i32, [pd, pg, pk, P, P, P]),
@@ -86,7 +88,8 @@ def load(path: str = LIB_PATH):
 
 EXPORTED = ("ckv_workspace_size", "ckv_centroids_from_rows", "ckv_centroids_to_rows",
             "ckv_score_centroids", "ckv_select", "ckv_sparse_decode_attn", "ckv_local_update",
-            "ckv_decode_step", "ckv_dense_workspace_size", "ckv_dense_decode_attn",
+            "ckv_decode_step", "ckv_decode_step_noalloc", "ckv_dense_workspace_size",
+            "ckv_dense_decode_attn",
             "ckv_rebuild_centroids", "ckv_centroid_drift", "ckv_prefill_edges",
             "ckv_status_string")
 
@@ -230,6 +233,27 @@ def ckv_decode_step(dims, q, k_new, v_new, graphs, kv, budget, n_cand, scale, sc
                                   _stream(stream)), "ckv_decode_step")
 
 
+def ckv_decode_step_noalloc(dims, q, k_new, v_new, graphs, kv, budget, n_cand, scale, scores,
+                            index_list, index_len, num_selected, cand, selected, assigned, out,
+                            err_flag, events=None, stream=None):
+    """ckv_decode_step without a workspace argument: the library's own device array."""
+    ev = None
+    if events is not None:
+        if len(events) != 8:
+            raise CkvError("ckv_decode_step_noalloc takes 8 timing events")
+        for e in events:
+            if e.cuda_event == 0:
+                e.record()
+        ev = (C.c_void_p * 8)(*[e.cuda_event for e in events])
+    _check(load().ckv_decode_step_noalloc(C.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                          C.byref(graphs), C.byref(kv), _ptr(budget), n_cand,
+                                          scale, _ptr(scores), _ptr(index_list),
+                                          index_list.shape[1], _ptr(index_len),
+                                          _ptr(num_selected), _ptr(cand), _ptr(selected),
+                                          _ptr(assigned), _ptr(out), _ptr(err_flag), ev,
+                                          _stream(stream)), "ckv_decode_step_noalloc")
+
+
 def ckv_status_string(status: int) -> str:
     return load().ckv_status_string(status).decode()
 
@@ -339,6 +363,13 @@ class DecodeLayer:
                         scale, self.scores, self.index_list, self.index_len, self.num_selected,
                         self.cand, self.selected, self.assigned, self.out, self.ws, self.err,
                         events=events)
+
+    def step_noalloc(self, q, k_new, v_new, scale, events=None):
+        """The same step through ckv_decode_step_noalloc (no workspace argument)."""
+        ckv_decode_step_noalloc(self.dims, q, k_new, v_new, self.graphs, self.kv, self.budget,
+                                self.M, scale, self.scores, self.index_list, self.index_len,
+                                self.num_selected, self.cand, self.selected, self.assigned,
+                                self.out, self.err, events=events)
 
     def centroid_rows(self) -> torch.Tensor:
         rows = torch.empty((self.NG, self.Cmax, self.cdim), dtype=torch.float32,

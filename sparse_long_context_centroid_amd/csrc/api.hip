@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "ckv.h"
 #include "ckv_internal.h"
@@ -226,13 +227,19 @@ ckv_status ckv_local_update(const ckv_dims *dims, const void *k_new, const void 
                                          err_flag, static_cast<hipStream_t>(stream)));
 }
 
-ckv_status ckv_decode_step(const ckv_dims *dims, const void *q, const void *k_new,
-                           const void *v_new, const ckv_graphs *graphs, const ckv_kv *kv,
-                           const int32_t *budget, int32_t n_cand, float scale, float *scores,
-                           int32_t *index_list, int32_t index_stride, int32_t *index_len,
-                           int32_t *num_selected, int32_t *cand, uint8_t *selected,
-                           int32_t *assigned, float *out, void *ws, size_t ws_bytes,
-                           int32_t *err_flag, void *const *events, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode step behind ckv_decode_step and ckv_decode_step_noalloc; ws holds
+// ws_bytes of device scratch.
+ckv_status decode_step_impl(const ckv_dims *dims, const void *q, const void *k_new,
+                            const void *v_new, const ckv_graphs *graphs, const ckv_kv *kv,
+                            const int32_t *budget, int32_t n_cand, float scale, float *scores,
+                            int32_t *index_list, int32_t index_stride, int32_t *index_len,
+                            int32_t *num_selected, int32_t *cand, uint8_t *selected,
+                            int32_t *assigned, float *out, void *ws, size_t ws_bytes,
+                            int32_t *err_flag, void *const *events, void *stream) {
     Problem p;
     ckv_status s = make_problem(dims, p);
     if (s != CKV_OK) return s;
@@ -284,6 +291,69 @@ ckv_status ckv_decode_step(const ckv_dims *dims, const void *q, const void *k_ne
         return s;
     return hip_status(ckv::launch_attn_merge(timed(3), index_stride, out,
                                              static_cast<float *>(ws), kv->seq_len, st));
+}
+
+// Scratch of ckv_decode_step_noalloc: one array per GPU the library runs on, held
+// until the process ends.  In host code `scratch` only names the symbol; its
+// device address on each GPU comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address reaches the kernels.
+constexpr size_t kNoallocScratchBytes = (size_t)CKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, looked up on the first call on that
+// device; nullptr on failure.
+void *device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+ckv_status ckv_decode_step(const ckv_dims *dims, const void *q, const void *k_new,
+                           const void *v_new, const ckv_graphs *graphs, const ckv_kv *kv,
+                           const int32_t *budget, int32_t n_cand, float scale, float *scores,
+                           int32_t *index_list, int32_t index_stride, int32_t *index_len,
+                           int32_t *num_selected, int32_t *cand, uint8_t *selected,
+                           int32_t *assigned, float *out, void *ws, size_t ws_bytes,
+                           int32_t *err_flag, void *const *events, void *stream) {
+    return decode_step_impl(dims, q, k_new, v_new, graphs, kv, budget, n_cand, scale, scores,
+                            index_list, index_stride, index_len, num_selected, cand, selected,
+                            assigned, out, ws, ws_bytes, err_flag, events, stream);
+}
+
+ckv_status ckv_decode_step_noalloc(const ckv_dims *dims, const void *q, const void *k_new,
+                                   const void *v_new, const ckv_graphs *graphs, const ckv_kv *kv,
+                                   const int32_t *budget, int32_t n_cand, float scale,
+                                   float *scores, int32_t *index_list, int32_t index_stride,
+                                   int32_t *index_len, int32_t *num_selected, int32_t *cand,
+                                   uint8_t *selected, int32_t *assigned, float *out,
+                                   int32_t *err_flag, void *const *events, void *stream) {
+    // the size check needs no device: a step whose scratch exceeds the array is
+    // refused before anything is looked up or enqueued
+    const size_t need = ckv_workspace_size(dims, index_stride);
+    if (need == 0) {
+        Problem p;
+        const ckv_status s = make_problem(dims, p);
+        return s != CKV_OK ? s : CKV_ERR_INVALID_ARG;
+    }
+    if (need > kNoallocScratchBytes) return CKV_ERR_WORKSPACE;
+    void *ws = device_scratch();
+    if (!ws) return CKV_ERR_HIP;
+    return decode_step_impl(dims, q, k_new, v_new, graphs, kv, budget, n_cand, scale, scores,
+                            index_list, index_stride, index_len, num_selected, cand, selected,
+                            assigned, out, ws, kNoallocScratchBytes, err_flag, events, stream);
 }
 
 const char *ckv_status_string(ckv_status status) {

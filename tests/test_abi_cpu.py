@@ -120,6 +120,22 @@ def test_empty_member_pool_passes_validation(lib):
                                 fake, None) == -1
 
 
+def test_noalloc_step_refuses_oversized_scratch(lib):
+    """ckv_decode_step_noalloc checks the step's scratch against its array's size
+    before touching the device: 512 graphs x 86 splits need more than it holds."""
+    d = dims(B=64)
+    fake = C.c_void_p(0x1000)
+    g = Bd.ckv_graphs(fake, fake, fake, fake, fake, fake)
+    kv = Bd.ckv_kv(fake, fake, fake, 16, 8, 8, fake)
+    assert lib.ckv_workspace_size(C.byref(d), 16388) > 32 << 20
+    assert lib.ckv_decode_step_noalloc(C.byref(d), fake, fake, fake, C.byref(g), C.byref(kv),
+                                       fake, 8, 0.1, fake, fake, 16388, fake, None, fake, None,
+                                       fake, fake, fake, None, None) == -3
+    assert lib.ckv_decode_step_noalloc(C.byref(dims(d=96)), fake, fake, fake, C.byref(g),
+                                       C.byref(kv), fake, 8, 0.1, fake, fake, 16388, fake, None,
+                                       fake, None, fake, fake, fake, None, None) == -2
+
+
 def test_dense_entry_points_validate(lib):
     d = dims(B=4)
     fake = C.c_void_p(0x1000)
