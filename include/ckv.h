@@ -75,7 +75,7 @@ enum {
 };
 
 /* Largest supported values. */
-enum { CKV_MAX_COMMS = 4096, CKV_MAX_CAND = 16, CKV_MAX_EDGES = 8 };
+enum { CKV_MAX_COMMS = 8192, CKV_MAX_CAND = 16, CKV_MAX_EDGES = 8 };
 
 typedef struct ckv_dims {
     int32_t batch;         /* B sequences                                          */

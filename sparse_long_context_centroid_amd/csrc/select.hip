@@ -204,8 +204,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int32_t *__restrict__ err) {
     __shared__ int red[2][6 * kSelWaves];
     __shared__ int scan_tmp[2 * kSelWaves];
-    __shared__ int list_start[CKV_MAX_COMMS];
-    __shared__ int list_off[CKV_MAX_COMMS + 1];
+    // kept communities of the graph (at most IPT per thread), in id order
+    __shared__ int list_start[IPT * kSelThreads];
+    __shared__ int list_off[IPT * kSelThreads + 1];
     __shared__ int s_src[kSelSrcMax];
     __shared__ uint32_t cand_key[CKV_MAX_CAND];
     __shared__ int cand_id[CKV_MAX_CAND];
@@ -548,7 +549,9 @@ hipError_t launch_select(const Problem &p, const float *scores, const ckv_graphs
                            idx_len, num_sel, cand, selected, err);                              \
         return hipGetLastError();                                                               \
     }
+    static_assert(CKV_MAX_COMMS <= 8 * kSelThreads, "instances up to the community cap");
     CKV_SEL_CASE(1) CKV_SEL_CASE(2) CKV_SEL_CASE(3) CKV_SEL_CASE(4)
+    CKV_SEL_CASE(6) CKV_SEL_CASE(8)
 #undef CKV_SEL_CASE
     return hipErrorInvalidValue;
 }

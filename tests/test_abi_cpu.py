@@ -58,7 +58,7 @@ def test_workspace_sizes(lib):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(d=96), -2), (dict(Hq=30), -1), (dict(Hq=48, Hkv=4), -2), (dict(gpk=2), -1),
-    (dict(Cmax=100), -1), (dict(Cmax=8192), -2), (dict(dtype=7), -2), (dict(B=0), -1),
+    (dict(Cmax=100), -1), (dict(Cmax=8256), -2), (dict(dtype=7), -2), (dict(B=0), -1),
     (dict(S=-1), -1),
 ])
 def test_bad_dims_rejected(lib, kw, status):

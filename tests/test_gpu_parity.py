@@ -285,13 +285,25 @@ def test_parity_empty_communities(fused):
 
 
 def test_parity_maximum_sizes():
-    """Near the largest community count (one 250K-token sequence: ~3900
-    communities, eight per select thread), the largest candidate count (16) and a
-    16K budget (86 attention splits per graph, past one merge load round)."""
+    """A long sequence (250K tokens: ~3900 communities, four per select thread),
+    the largest candidate count (16) and a 16K budget (86 attention splits per
+    graph, past one merge load round)."""
     _case("maximum sizes")
     spec = I.ConfigSpec("max-sizes", 1, 4, 1, 128, 250000, False, 16384, 2, I.DT_BF16,
                         n_cand=16)
     wl = I.make_workload(spec, device="cuda")
     assert wl.Cmax > 3584 and wl.Cmax <= 4096
+    run_parity(wl, fused=True)
+    run_parity(I.make_workload(spec, device="cuda"), fused=False)
+
+
+def test_parity_community_cap():
+    """Near the community cap (8192 per graph): 128K tokens over ~8100 communities,
+    a mean community size of 16, eight communities per select thread."""
+    _case("community cap")
+    spec = I.ConfigSpec("comm-cap", 1, 8, 2, 128, 131072, False, 4096, 2, I.DT_BF16,
+                        markov_labels=8100)
+    wl = I.make_workload(spec, device="cuda")
+    assert 7168 < wl.Cmax <= 8192
     run_parity(wl, fused=True)
     run_parity(I.make_workload(spec, device="cuda"), fused=False)
