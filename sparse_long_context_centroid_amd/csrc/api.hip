@@ -2,6 +2,7 @@
 // launches on the caller's stream.  No allocation, no synchronisation, no state.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <mutex>
 
@@ -9,6 +10,22 @@
 #include "ckv_internal.h"
 
 using ckv::Problem;
+
+namespace ckv {
+int device_cu_count() {
+    constexpr int kDevices = 64;
+    static std::atomic<int> cache[kDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+}  // namespace ckv
 
 namespace {
 

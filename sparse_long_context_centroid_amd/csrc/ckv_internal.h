@@ -43,6 +43,10 @@ inline int attn_max_splits(const Problem &p, int index_stride) {
     return (index_stride + ch - 1) / ch;
 }
 
+// Compute units of the current device (queried once per device; 256, the MI355X
+// count, if the query fails).
+int device_cu_count();
+
 inline int log2_pow2(int x) {
     int l = 0;
     while ((1 << l) < x) ++l;

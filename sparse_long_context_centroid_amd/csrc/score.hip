@@ -24,8 +24,13 @@ namespace ckv {
 // lines over every CU, and the query staging needs no workgroup barrier.
 constexpr int kScoreThreads = 64;
 // float4 chunks of a centroid in flight per lane: the next chunk's loads are
-// issued before the current one is consumed (two chunks of registers).
+// issued before the current one is consumed (two chunks of registers).  A grid of
+// at most one wave per SIMD streams 8-float4 chunks; a larger grid (several
+// rounds of waves) takes 4-float4 chunks: its rounds overlap anyway, and a
+// workgroup past its graph's community count (ragged batches) fetches half as
+// much before it learns that and leaves.
 constexpr int kScoreChunk = 8;
+constexpr int kScoreChunkRounds = 4;
 
 // v_fmac_f64 whose first factor comes from lane N of this lane's 16-lane row (DPP
 // row_newbcast, a gfx90a+ 64-bit DPP control): acc = q[row lane N] * m + acc with
@@ -68,12 +73,11 @@ __device__ __forceinline__ void score_chunk(double (&acc)[GH], const double (&qr
 // of the chunk's values (lane p of a 16-lane row: values p, 16 + p, ...), and the
 // FMAs take each value from its row lane with a DPP broadcast: the chunk costs a
 // few LDS reads per lane instead of one broadcast LDS read per value.
-template <typename T, int D, int GH>
+template <typename T, int D, int GH, int KC>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const T *__restrict__ q, const float *__restrict__ cent, const int32_t *__restrict__ num_comms,
     const int32_t *__restrict__ comm_size, int Cmax, int Hq, int Hkv, int gpk, double scale,
     float *__restrict__ scores) {
-    constexpr int KC = kScoreChunk;
     static_assert((D / 4) % KC == 0, "whole chunks");
     // lane j stages elements 4k..4k+3 of head h, k = j / GH, h = j % GH, with one
     // vector load
@@ -291,11 +295,13 @@ __global__ void interleaved_to_rows_kernel(const float *__restrict__ cent, float
 template <typename T, int D, int GH>
 static void launch_score_t(const Problem &p, const void *q, const ckv_graphs &gr, double scale,
                            float *scores, hipStream_t st) {
-    hipExtLaunchKernelGGL((score_kernel<T, D, GH>),
-                          dim3((p.Cmax + kScoreThreads - 1) / kScoreThreads, p.NG()),
-                          dim3(kScoreThreads), 0, st, p.ev_start, p.ev_stop, 0,
-                          static_cast<const T *>(q), gr.centroids,
-                       gr.num_comms, gr.comm_size, p.Cmax, p.Hq, p.Hkv, p.gpk, scale, scores);
+    const dim3 grid((p.Cmax + kScoreThreads - 1) / kScoreThreads, p.NG());
+    const bool rounds = (long long)grid.x * grid.y > 4LL * device_cu_count();
+    auto kernel = rounds ? score_kernel<T, D, GH, kScoreChunkRounds>
+                         : score_kernel<T, D, GH, kScoreChunk>;
+    hipExtLaunchKernelGGL(kernel, grid, dim3(kScoreThreads), 0, st, p.ev_start, p.ev_stop, 0,
+                          static_cast<const T *>(q), gr.centroids, gr.num_comms, gr.comm_size,
+                          p.Cmax, p.Hq, p.Hkv, p.gpk, scale, scores);
 }
 
 template <typename T, int D, int GH>
