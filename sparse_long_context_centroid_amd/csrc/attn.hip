@@ -40,6 +40,14 @@
 //   partials: m* = max m_s, l = sum l_s 2^(m_s-m*), o = sum acc_s 2^(m_s-m*) / l.
 // * In the fused decode step grid row 0 holds extra workgroups, one wave per
 //   graph, that run the local update while the other workgroups stream K/V.
+// * A list grid that needs several rounds of resident workgroups (ragged batches:
+//   many short lists and a few long ones) runs as one persistent round instead:
+//   `workers` workgroups (the launch's capacity) each build the compact list of
+//   busy splits (graph g owns items pfx[g] .. pfx[g+1]-1, from the list lengths)
+//   and walk it with stride `workers`, after marking the grid's empty split slots
+//   for the merge.  No workgroup is dispatched for an empty split, and every slot
+//   keeps a busy workgroup until the list runs out.
+#include <atomic>
 #include <type_traits>
 
 #include "ckv_device.h"
@@ -155,7 +163,7 @@ enum AttnMode {
     kAttnDense = 2           // every cached token 0..seq_len-1 (the dense baseline)
 };
 
-template <typename T, int D, int GH, int MODE>
+template <typename T, int D, int GH, int MODE, bool PERSIST>
 __global__ __launch_bounds__(256) void attn_kernel(
     const T *__restrict__ q, T *__restrict__ kc, T *__restrict__ vc,
     const int32_t *__restrict__ page_table, int log2ps, int max_pages, int num_pages,
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
     int list_div, const int32_t *__restrict__ idx_len, int Hq, int Hkv, int gpk,
     float scale_log2,
     float *__restrict__ part, int max_splits, int chunks_per_wg, int32_t *__restrict__ err,
-    UpdateArgs u) {
+    UpdateArgs u, int n_graphs, int workers) {
     constexpr int EPL = 16 / sizeof(T);     // row elements per lane
     constexpr int LPR = D / EPL;            // lanes per row
     constexpr int RPW = kWave / LPR;        // rows per wave-wide load
@@ -189,13 +197,22 @@ __global__ __launch_bounds__(256) void attn_kernel(
     // runs only the local update and uses the same memory for its candidate rows.
     constexpr int kStageFloats = kMfma ? kAttnWaves * 16 * D / 2 + GH * D / 2 : 1;
     constexpr int kUpdFloats = MODE == kAttnIndexedUpdate ? kAttnWaves * kUpdLdsFloats(D) : 1;
-    __shared__ __align__(16) float s_big[kStageFloats > kUpdFloats ? kStageFloats : kUpdFloats];
+    // persistent grid: the busy-split prefix and list length of every graph, after
+    // the stage (the update rows' staging overlaps them; those workgroups do no
+    // attention)
+    constexpr int kPfxInts = PERSIST ? 2 * kAttnPersistMaxGraphs + 1 : 0;
+    constexpr int kWorkFloats = kStageFloats + kPfxInts;
+    __shared__ __align__(16) float s_big[kWorkFloats > kUpdFloats ? kWorkFloats : kUpdFloats];
+    __shared__ int s_wsum[kAttnWaves];
+    constexpr bool persist = PERSIST;
+    static_assert(!PERSIST || MODE != kAttnDense, "the dense grid is always direct");
 
     if constexpr (MODE == kAttnIndexedUpdate) {
         // grid row 0: the local update, one wave per graph (dispatched first, so it
         // runs under the K/V stream of the attention workgroups); seq_len advances
         // in the merge launch
-        if (blockIdx.y == 0) {
+        // direct grid: row 0; persistent grid: the workgroups before the workers
+        if (persist ? (int)blockIdx.x < (int)gridDim.x - workers : blockIdx.y == 0) {
             const int w = threadIdx.x / kWave;
             const size_t gu = (size_t)blockIdx.x * kAttnWaves + w;
             if (gu < u.NG)
@@ -208,23 +225,94 @@ __global__ __launch_bounds__(256) void attn_kernel(
             return;
         }
     }
-    const int NG = gridDim.x;
-    const int g = graph_of_column(blockIdx.x, NG, gpk);
-    const int split = (int)blockIdx.y - (MODE == kAttnIndexedUpdate ? 1 : 0);
+    const int NG = n_graphs;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
     const int G = Hq / Hkv;
+    const int span = CH * chunks_per_wg;  // tokens one workgroup may cover
+    int *s_pfx = reinterpret_cast<int *>(s_big + kStageFloats);  // [NG + 1]
+    int *s_len = s_pfx + kAttnPersistMaxGraphs + 1;               // [NG]
+    int item = 0, item_end = 1, item_step = 1;
+    if (persist) {
+        // list lengths and split counts of all graphs, kPT consecutive graphs per
+        // thread, and their exclusive prefix over the workgroup (wave scans by
+        // shuffles, then the wave totals)
+        constexpr int kPT = (kAttnPersistMaxGraphs + 255) / 256;
+        int lens[kPT], cnt[kPT], tsum = 0;
+#pragma unroll
+        for (int j = 0; j < kPT; ++j) {
+            const int gg = tid * kPT + j;
+            const int L = gg < NG ? min(idx_len[gg / list_div], idx_stride) : 0;
+            lens[j] = L;
+            cnt[j] = (L + span - 1) / span;
+            tsum += cnt[j];
+        }
+        int incl = tsum;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int v = __shfl_up(incl, o);
+            incl += lane >= o ? v : 0;
+        }
+        if (lane == kWave - 1) s_wsum[w] = incl;
+        __syncthreads();
+        int off = incl - tsum;
+        for (int v = 0; v < w; ++v) off += s_wsum[v];
+#pragma unroll
+        for (int j = 0; j < kPT; ++j) {
+            const int gg = tid * kPT + j;
+            if (gg < NG) {
+                s_pfx[gg] = off;
+                s_len[gg] = lens[j];
+            }
+            off += cnt[j];
+        }
+        if (tid == blockDim.x - 1) s_pfx[NG] = off;  // every busy split of the grid
+        __syncthreads();
+        // empty split slots keep a weight-0 partial for the merge, as in the direct
+        // grid; each slot is marked by one thread of the workers
+        const int worker = (int)blockIdx.x - ((int)gridDim.x - workers);
+        for (int sl = worker * (int)blockDim.x + tid; sl < NG * max_splits;
+             sl += workers * (int)blockDim.x) {
+            const int gg = sl / max_splits, sp = sl % max_splits;
+            if (sp >= s_pfx[gg + 1] - s_pfx[gg]) {
+#pragma unroll
+                for (int h = 0; h < GH; ++h) {
+                    float *pp = part + (((size_t)gg * GH + h) * max_splits + sp) * (D + 2);
+                    pp[0] = -__builtin_inff();
+                    pp[1] = 0.f;
+                }
+            }
+        }
+        item = worker;
+        item_end = s_pfx[NG];
+        item_step = workers;
+    }
+    for (; item < item_end; item += item_step) {
+    int g, split;
+    if (persist) {
+        // the graph whose items hold this one: the last g with pfx[g] <= item
+        int lo = 0, hi = NG;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_pfx[mid] <= item) lo = mid;
+            else hi = mid;
+        }
+        g = lo;
+        split = item - s_pfx[g];
+    } else {
+        g = graph_of_column(blockIdx.x, NG, gpk);
+        split = (int)blockIdx.y - (MODE == kAttnIndexedUpdate ? 1 : 0);
+    }
     const int b = g / (Hkv * gpk);
     const int kvh = (g / gpk) % Hkv;
     const int h0 = kvh * G + (gpk == 1 ? 0 : g % gpk);
     const int n = seq_len[b];
     // index list of this graph (one list serves list_div consecutive graphs)
     const int gl = g / list_div;
-    const int len = MODE == kAttnDense ? n : min(idx_len[gl], idx_stride);
-    const int span = CH * chunks_per_wg;  // tokens one workgroup may cover
+    const int len = persist ? s_len[g] : MODE == kAttnDense ? n : min(idx_len[gl], idx_stride);
     const int nsplit = (len + span - 1) / span;
-    if (split >= nsplit) {
+    if (!persist && split >= nsplit) {
         // an empty split still marks its partial (weight 0) so the merge can read
         // every split without knowing the list length
         if (tid < GH) {
@@ -730,6 +818,8 @@ __global__ __launch_bounds__(256) void attn_kernel(
             pp[1] = ll;
         }
     }
+    if (persist) __syncthreads();  // the next item reuses the workgroup's LDS
+    }
 }
 
 // Merge of one graph's split partials into out (m* = max m_s, weights
@@ -829,18 +919,59 @@ __global__ __launch_bounds__(512) void merge_kernel(int Hq, int Hkv, int gpk,
     merge_graph<D, GH>(blockIdx.x, Hq, Hkv, gpk, out, part, max_splits, s_w);
 }
 
+// Workgroups of attn_kernel<T, D, GH, MODE> resident on the current device at
+// once (queried once per device and instance; 0 if the query fails).
+template <typename T, int D, int GH, int MODE>
+static int attn_persist_capacity() {
+    constexpr int kDevices = 64;
+    static std::atomic<int> cache[kDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 0;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<T, D, GH, MODE, true>,
+                                                     256, 0) != hipSuccess ||
+        per_cu <= 0)
+        return 0;
+    c = per_cu * device_cu_count();
+    cache[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
 template <typename T, int D, int GH, int MODE>
 static void launch_partials_t(const Problem &p, const void *q, const ckv_kv &kv,
                               const int32_t *idx, int idx_stride, const int32_t *idx_len,
                               float scale, float *partials, int32_t *err, const UpdateArgs &u,
                               int ms, int cpw, hipStream_t st) {
-    hipExtLaunchKernelGGL((attn_kernel<T, D, GH, MODE>),
-                          dim3(p.NG(), ms + (MODE == kAttnIndexedUpdate ? 1 : 0)), dim3(256), 0,
-                          st, p.ev_start, p.ev_stop, 0, static_cast<const T *>(q),
+    const int NG = p.NG();
+    const int upd_wgs = MODE == kAttnIndexedUpdate ? (NG + kAttnWaves - 1) / kAttnWaves : 0;
+    // a list grid larger than one round of resident workgroups runs persistent (group
+    // graphs only: per-head graphs keep the direct grid's column order, which puts
+    // the graphs of a KV head on one XCD)
+    if constexpr (MODE != kAttnDense) {
+        if (p.gpk == 1 && NG <= kAttnPersistMaxGraphs) {
+            const int cap = attn_persist_capacity<T, D, GH, MODE>();
+            if ((long long)NG * ms + upd_wgs > cap && cap > upd_wgs) {
+                const int workers = cap - upd_wgs;
+                hipExtLaunchKernelGGL(
+                    (attn_kernel<T, D, GH, MODE, true>), dim3(upd_wgs + workers), dim3(256), 0,
+                    st, p.ev_start, p.ev_stop, 0, static_cast<const T *>(q),
+                    static_cast<T *>(kv.k), static_cast<T *>(kv.v), kv.page_table,
+                    log2_pow2(kv.page_size), kv.max_pages_per_seq, kv.num_pages, kv.seq_len, idx,
+                    idx_stride, p.list_div, idx_len, p.Hq, p.Hkv, p.gpk, scale * kLog2e, partials,
+                    ms, cpw, err, u, NG, workers);
+                return;
+            }
+        }
+    }
+    hipExtLaunchKernelGGL((attn_kernel<T, D, GH, MODE, false>),
+                          dim3(NG, ms + (MODE == kAttnIndexedUpdate ? 1 : 0)), dim3(256), 0, st,
+                          p.ev_start, p.ev_stop, 0, static_cast<const T *>(q),
                           static_cast<T *>(kv.k), static_cast<T *>(kv.v), kv.page_table,
                           log2_pow2(kv.page_size), kv.max_pages_per_seq, kv.num_pages,
                           kv.seq_len, idx, idx_stride, p.list_div, idx_len, p.Hq, p.Hkv, p.gpk,
-                          scale * kLog2e, partials, ms, cpw, err, u);
+                          scale * kLog2e, partials, ms, cpw, err, u, NG, 0);
 }
 
 // One launcher for the three modes; GH = heads per graph of `p`.

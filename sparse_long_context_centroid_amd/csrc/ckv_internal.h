@@ -35,6 +35,9 @@ struct Problem {
 // so one load covers 1024/(d*elem) rows.  Tokens per workgroup:
 constexpr int kAttnWaves = 4;
 constexpr int kAttnLoads = 12;
+// Largest graph count of a persistent attention grid (its per-graph split prefix
+// lives in LDS); more graphs always take the direct grid.
+constexpr int kAttnPersistMaxGraphs = 1024;
 constexpr int attn_chunk(int D, int elem_bytes) {
     return kAttnWaves * kAttnLoads * (1024 / (D * elem_bytes));
 }

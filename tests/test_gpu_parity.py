@@ -307,3 +307,16 @@ def test_parity_community_cap():
     assert 7168 < wl.Cmax <= 8192
     run_parity(wl, fused=True)
     run_parity(I.make_workload(spec, device="cuda"), fused=False)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["four-calls", "fused-step"])
+def test_parity_persistent_attention_grid(fused):
+    """A list grid larger than one round of resident workgroups (64 group graphs x
+    22 splits) runs as the persistent attention grid; ragged contexts leave many
+    split slots empty."""
+    _case(f"persistent attention grid fused={fused}")
+    spec = I.ConfigSpec("persist-grid", 8, 32, 8, 128, 32768, False, 4096, 2, I.DT_BF16)
+    wl = I.make_workload(spec, device="cuda",
+                         contexts=[32768, 5000, 20000, 9000, 32768, 3000, 12000, 26000])
+    assert wl.NG * ((wl.S + int(wl.budget.max()) + 191) // 192) > 1024
+    run_parity(wl, fused=fused)
