@@ -320,3 +320,26 @@ def test_parity_persistent_attention_grid(fused):
                          contexts=[32768, 5000, 20000, 9000, 32768, 3000, 12000, 26000])
     assert wl.NG * ((wl.S + int(wl.budget.max()) + 191) // 192) > 1024
     run_parity(wl, fused=fused)
+
+
+def test_parity_persistent_grid_at_its_graph_limit():
+    """The persistent attention grid at its largest graph count (1024 group graphs:
+    128 sequences x 8 KV heads, every thread of the prologue holding 4 graphs), with
+    one- and two-split lists."""
+    _case("persistent grid, 1024 graphs")
+    spec = I.ConfigSpec("persist-1024", 128, 32, 8, 128, 600, False, 200, 2, I.DT_BF16)
+    rng = np.random.default_rng(5)
+    wl = I.make_workload(spec, device="cuda", contexts=[int(x) for x in rng.integers(150, 600, 128)])
+    assert wl.NG == 1024
+    run_parity(wl, fused=True)
+
+
+def test_parity_persistent_grid_with_every_list_empty():
+    """No sinks and a zero budget: every list is empty, the persistent grid has no
+    busy split (its workers only mark the empty slots) and every output is 0."""
+    _case("persistent grid, empty lists")
+    spec = I.ConfigSpec("persist-empty", 8, 32, 8, 128, 4096, False, 0, 2, I.DT_BF16,
+                        num_sinks=0)
+    wl = I.make_workload(spec, device="cuda")
+    s = run_parity(wl, fused=True, index_stride=4096)
+    assert s["mean_idx_len"] == 0
