@@ -287,19 +287,16 @@ ckv_status decode_step_impl(const ckv_dims *dims, const void *q, const void *k_n
                                            cand, selected, err_flag, st))) != CKV_OK)
         return s;
     if (p.layer()) {
-        // the layer graph: attention, then its own update launch (no bump), then the
-        // merge with the seq_len advance
+        // the layer graph: attention, then the merge with the update (and the seq_len
+        // advance) in extra workgroups of the same launch
         if ((s = hip_status(ckv::launch_attn_partials(timed(2), q, *kv, index_list,
                                                       index_stride, index_len, scale,
                                                       static_cast<float *>(ws), err_flag,
                                                       nullptr, st))) != CKV_OK)
             return s;
-        if ((s = hip_status(ckv::launch_layer_update(p, k_new, v_new, cand, n_cand, *graphs,
-                                                     *kv, assigned, err_flag, false, st))) !=
-            CKV_OK)
-            return s;
-        return hip_status(ckv::launch_attn_merge(timed(3), index_stride, out,
-                                                 static_cast<float *>(ws), kv->seq_len, st));
+        return hip_status(ckv::launch_attn_merge_layer_update(
+            timed(3), index_stride, out, static_cast<float *>(ws), k_new, v_new, cand, n_cand,
+            *graphs, *kv, assigned, err_flag, st));
     }
     const ckv::UpdateSpec upd{k_new, v_new, cand, n_cand, graphs, assigned};
     if ((s = hip_status(ckv::launch_attn_partials(timed(2), q, *kv, index_list, index_stride,

@@ -1032,6 +1032,45 @@ hipError_t launch_dense_partials(const Problem &p, const void *q, const ckv_kv &
                        UpdateArgs{}, ms, cpw, st);
 }
 
+// The layer graph's merge launch also runs the step's update: B extra workgroups,
+// one per sequence, each running the layer update (which advances its sequence's
+// seq_len itself, after reading n).  The update writes centroids, member lists and
+// K/V row n, none of which the merge reads; the merge reads only the partials.
+struct LayerUpdArgs {
+    const void *k_new, *v_new;
+    const int32_t *cand;
+    int M;
+    float *cent;
+    const int32_t *num_comms, *comm_start;
+    int32_t *comm_size;
+    const int32_t *comm_cap;
+    int32_t *members;
+    int Cmax, Hkv;
+    void *kc, *vc;
+    const int32_t *page_table;
+    int log2ps, max_pages, num_pages;
+    int32_t *seq_len, *assigned, *err;
+};
+
+template <typename T, int D, int GH>
+__global__ __launch_bounds__(512) void merge_layer_update_kernel(int Hq, int Hkv,
+                                                                 float *__restrict__ out,
+                                                                 const float *__restrict__ part,
+                                                                 int max_splits, int n_merge,
+                                                                 LayerUpdArgs a) {
+    extern __shared__ __align__(16) float s_dyn[];
+    if ((int)blockIdx.x >= n_merge) {
+        layer_update_seq<T, D>((int)blockIdx.x - n_merge, static_cast<const T *>(a.k_new),
+                               static_cast<const T *>(a.v_new), a.cand, a.M, a.cent,
+                               a.num_comms, a.comm_start, a.comm_size, a.comm_cap, a.members,
+                               a.Cmax, a.Hkv, static_cast<T *>(a.kc), static_cast<T *>(a.vc),
+                               a.page_table, a.log2ps, a.max_pages, a.num_pages, a.seq_len, 1,
+                               a.assigned, a.err, reinterpret_cast<unsigned char *>(s_dyn));
+        return;
+    }
+    merge_graph<D, GH>(blockIdx.x, Hq, Hkv, 1, out, part, max_splits, s_dyn);
+}
+
 static hipError_t launch_merge(const Problem &p, int ms, float *out, const float *partials,
                                int32_t *bump_seq_len, hipStream_t st) {
     const int GH = p.heads_per_graph();
@@ -1059,6 +1098,41 @@ hipError_t launch_dense_merge(const Problem &p, const ckv_kv &kv, float *out,
     const Problem pd = dense_problem(p);
     int cpw = 1;
     return launch_merge(pd, dense_max_splits(pd, kv, &cpw), out, partials, nullptr, st);
+}
+
+hipError_t launch_attn_merge_layer_update(const Problem &pg, int idx_stride, float *out,
+                                         const float *partials, const void *k_new,
+                                         const void *v_new, const int32_t *cand, int n_cand,
+                                         const ckv_graphs &gr, const ckv_kv &kv,
+                                         int32_t *assigned, int32_t *err, hipStream_t st) {
+    if (!pg.layer() || !layer_update_fits(pg, n_cand)) return hipErrorInvalidValue;
+    const Problem p = attn_problem(pg);
+    const int ms = attn_max_splits(p, idx_stride);
+    const int GH = p.heads_per_graph();
+    const size_t merge_lds = (size_t)GH * ms * sizeof(float);
+    const size_t upd_lds = layer_update_lds(pg.cdim(), n_cand);
+    const size_t lds = merge_lds > upd_lds ? merge_lds : upd_lds;
+    const LayerUpdArgs a{k_new, v_new, cand, n_cand, gr.centroids, gr.num_comms, gr.comm_start,
+                         gr.comm_size, gr.comm_cap, gr.members, pg.Cmax, pg.Hkv, kv.k, kv.v,
+                         kv.page_table, log2_pow2(kv.page_size), kv.max_pages_per_seq,
+                         kv.num_pages, kv.seq_len, assigned, err};
+#define CKV_MLU_CASE(TT, DT, DD, HH)                                                           \
+    if (p.dtype == DT && p.D == DD && GH == HH) {                                              \
+        hipExtLaunchKernelGGL((merge_layer_update_kernel<TT, DD, HH>), dim3(p.NG() + pg.B),    \
+                              dim3(512), lds, st, p.ev_start, p.ev_stop, 0, p.Hq, p.Hkv, out,   \
+                              partials, ms, p.NG(), a);                                        \
+        return hipGetLastError();                                                              \
+    }
+    CKV_MLU_CASE(bf16_t, CKV_DT_BF16, 128, 1) CKV_MLU_CASE(bf16_t, CKV_DT_BF16, 128, 2)
+    CKV_MLU_CASE(bf16_t, CKV_DT_BF16, 128, 4) CKV_MLU_CASE(bf16_t, CKV_DT_BF16, 128, 8)
+    CKV_MLU_CASE(bf16_t, CKV_DT_BF16, 64, 1) CKV_MLU_CASE(bf16_t, CKV_DT_BF16, 64, 2)
+    CKV_MLU_CASE(bf16_t, CKV_DT_BF16, 64, 4) CKV_MLU_CASE(bf16_t, CKV_DT_BF16, 64, 8)
+    CKV_MLU_CASE(float, CKV_DT_F32, 128, 1) CKV_MLU_CASE(float, CKV_DT_F32, 128, 2)
+    CKV_MLU_CASE(float, CKV_DT_F32, 128, 4) CKV_MLU_CASE(float, CKV_DT_F32, 128, 8)
+    CKV_MLU_CASE(float, CKV_DT_F32, 64, 1) CKV_MLU_CASE(float, CKV_DT_F32, 64, 2)
+    CKV_MLU_CASE(float, CKV_DT_F32, 64, 4) CKV_MLU_CASE(float, CKV_DT_F32, 64, 8)
+#undef CKV_MLU_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace ckv

@@ -120,6 +120,13 @@ hipError_t launch_attn_partials(const Problem &p, const void *q, const ckv_kv &k
                                 hipStream_t st);
 hipError_t launch_attn_merge(const Problem &p, int idx_stride, float *out, const float *partials,
                              int32_t *bump_seq_len, hipStream_t st);
+// The layer graph's merge with the step's layer update in extra workgroups (one per
+// sequence; each advances its seq_len).
+hipError_t launch_attn_merge_layer_update(const Problem &p, int idx_stride, float *out,
+                                         const float *partials, const void *k_new,
+                                         const void *v_new, const int32_t *cand, int n_cand,
+                                         const ckv_graphs &gr, const ckv_kv &kv,
+                                         int32_t *assigned, int32_t *err, hipStream_t st);
 // Dense baseline: attention over every cached token of each sequence.
 hipError_t launch_dense_partials(const Problem &p, const void *q, const ckv_kv &kv, float scale,
                                  float *partials, int32_t *err, hipStream_t st);
