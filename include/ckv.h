@@ -316,10 +316,11 @@ CKV_API ckv_status ckv_prefill_edges(const ckv_dims *dims, const void *q, const 
  * start / stop pair of each of the 4 kernels in the order above, bound to the
  * kernel's own execution (hipExtLaunchKernelGGL), so hipEventElapsedTime of a
  * pair is that kernel's duration without launch gaps.
- * The layer graph (graphs_per_kv = 0) also takes 4 launches: its update, whose
- * row staging does not fit the attention launch, runs in extra workgroups of the
- * merge launch (one per sequence, each advancing its seq_len), so the merge's
- * event pair covers it.
+ * The layer graph (graphs_per_kv = 0) also takes 4 launches: its update runs in
+ * extra workgroups of the attention launch, one per sequence, when its staging (the
+ * n_cand candidate rows of Hkv*d floats) fits there, as for d = 128, Hkv <= 8 and
+ * n_cand <= 8; otherwise in extra workgroups of the merge launch (each advancing
+ * its sequence's seq_len), whose event pair then covers it.
  */
 CKV_API ckv_status ckv_decode_step(const ckv_dims *dims, const void *q, const void *k_new,
                                    const void *v_new, const ckv_graphs *graphs, const ckv_kv *kv,

@@ -287,8 +287,19 @@ ckv_status decode_step_impl(const ckv_dims *dims, const void *q, const void *k_n
                                            cand, selected, err_flag, st))) != CKV_OK)
         return s;
     if (p.layer()) {
-        // the layer graph: attention, then the merge with the update (and the seq_len
-        // advance) in extra workgroups of the same launch
+        // the layer graph: its update runs in extra workgroups of the attention launch
+        // when its staging fits there (then the merge advances seq_len), else in extra
+        // workgroups of the merge launch (each advancing its sequence's seq_len)
+        if (ckv::layer_update_in_attention_fits(p, n_cand)) {
+            const ckv::UpdateSpec lupd{k_new, v_new, cand, n_cand, graphs, assigned};
+            if ((s = hip_status(ckv::launch_attn_partials(timed(2), q, *kv, index_list,
+                                                          index_stride, index_len, scale,
+                                                          static_cast<float *>(ws), err_flag,
+                                                          &lupd, st))) != CKV_OK)
+                return s;
+            return hip_status(ckv::launch_attn_merge(timed(3), index_stride, out,
+                                                     static_cast<float *>(ws), kv->seq_len, st));
+        }
         if ((s = hip_status(ckv::launch_attn_partials(timed(2), q, *kv, index_list,
                                                       index_stride, index_len, scale,
                                                       static_cast<float *>(ws), err_flag,

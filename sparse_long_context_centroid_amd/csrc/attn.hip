@@ -154,6 +154,9 @@ struct UpdateArgs {
     int32_t *members;
     int Cmax, NG;
     int32_t *assigned;
+    // the layer graph: NG sequences, one update workgroup each (layer_update_seq,
+    // its LDS from the update rows' staging area)
+    int layer;
 };
 
 // What a launch of attn_kernel reads as its token list.
@@ -213,6 +216,16 @@ __global__ __launch_bounds__(256) void attn_kernel(
         // in the merge launch
         // direct grid: row 0; persistent grid: the workgroups before the workers
         if (persist ? (int)blockIdx.x < (int)gridDim.x - workers : blockIdx.y == 0) {
+            if (u.layer) {
+                if ((int)blockIdx.x < u.NG)
+                    layer_update_seq<T, D>(
+                        blockIdx.x, static_cast<const T *>(u.k_new),
+                        static_cast<const T *>(u.v_new), u.cand, u.M, u.cent, u.num_comms,
+                        u.comm_start, u.comm_size, u.comm_cap, u.members, u.Cmax, Hkv, kc, vc,
+                        page_table, log2ps, max_pages, num_pages, seq_len, 0, u.assigned, err,
+                        reinterpret_cast<unsigned char *>(s_big));
+                return;
+            }
             const int w = threadIdx.x / kWave;
             const size_t gu = (size_t)blockIdx.x * kAttnWaves + w;
             if (gu < u.NG)
@@ -945,7 +958,9 @@ static void launch_partials_t(const Problem &p, const void *q, const ckv_kv &kv,
                               float scale, float *partials, int32_t *err, const UpdateArgs &u,
                               int ms, int cpw, hipStream_t st) {
     const int NG = p.NG();
-    const int upd_wgs = MODE == kAttnIndexedUpdate ? (NG + kAttnWaves - 1) / kAttnWaves : 0;
+    const int upd_wgs = MODE != kAttnIndexedUpdate ? 0
+                        : u.layer                  ? u.NG
+                                                   : (NG + kAttnWaves - 1) / kAttnWaves;
     // a list grid larger than one round of resident workgroups runs persistent (group
     // graphs only: per-head graphs keep the direct grid's column order, which puts
     // the graphs of a KV head on one XCD)
@@ -1006,18 +1021,28 @@ static hipError_t launch_mode(const Problem &p, int mode, const void *q, const c
     return hipErrorInvalidValue;
 }
 
+bool layer_update_in_attention_fits(const Problem &p, int n_cand) {
+    // the update rows' staging area of the attention launch: kAttnWaves wave slots
+    const size_t area = (size_t)kAttnWaves * kUpdLdsFloats(p.D) * sizeof(float);
+    return p.layer() && layer_update_fits(p, n_cand) &&
+           layer_update_lds(p.cdim(), n_cand, p.Hkv) <= area;
+}
+
 hipError_t launch_attn_partials(const Problem &pg, const void *q, const ckv_kv &kv,
                                 const int32_t *idx, int idx_stride, const int32_t *idx_len,
                                 float scale, float *partials, int32_t *err, const UpdateSpec *upd,
                                 hipStream_t st) {
-    if (upd && pg.layer()) return hipErrorInvalidValue;  // the layer graph updates apart
+    // the layer graph's update runs here only when its staging fits the launch's
+    // update rows (else the merge launch takes it)
+    if (upd && pg.layer() && !layer_update_in_attention_fits(pg, upd->n_cand))
+        return hipErrorInvalidValue;
     const Problem p = attn_problem(pg);
     UpdateArgs u{};
     if (upd) {
         u = UpdateArgs{upd->k_new, upd->v_new, upd->cand, upd->n_cand, upd->graphs->centroids,
                        upd->graphs->num_comms, upd->graphs->comm_start, upd->graphs->comm_size,
-                       upd->graphs->comm_cap, upd->graphs->members, p.Cmax, p.NG(),
-                       upd->assigned};
+                       upd->graphs->comm_cap, upd->graphs->members, p.Cmax,
+                       pg.layer() ? pg.B : p.NG(), upd->assigned, pg.layer() ? 1 : 0};
     }
     return launch_mode(p, upd ? kAttnIndexedUpdate : kAttnIndexed, q, kv, idx, idx_stride,
                        idx_len, scale, partials, err, u, attn_max_splits(p, idx_stride), 1, st);
@@ -1110,7 +1135,7 @@ hipError_t launch_attn_merge_layer_update(const Problem &pg, int idx_stride, flo
     const int ms = attn_max_splits(p, idx_stride);
     const int GH = p.heads_per_graph();
     const size_t merge_lds = (size_t)GH * ms * sizeof(float);
-    const size_t upd_lds = layer_update_lds(pg.cdim(), n_cand);
+    const size_t upd_lds = layer_update_lds(pg.cdim(), n_cand, pg.Hkv);
     const size_t lds = merge_lds > upd_lds ? merge_lds : upd_lds;
     const LayerUpdArgs a{k_new, v_new, cand, n_cand, gr.centroids, gr.num_comms, gr.comm_start,
                          gr.comm_size, gr.comm_cap, gr.members, pg.Cmax, pg.Hkv, kv.k, kv.v,

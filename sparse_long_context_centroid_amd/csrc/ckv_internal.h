@@ -120,8 +120,11 @@ hipError_t launch_attn_partials(const Problem &p, const void *q, const ckv_kv &k
                                 hipStream_t st);
 hipError_t launch_attn_merge(const Problem &p, int idx_stride, float *out, const float *partials,
                              int32_t *bump_seq_len, hipStream_t st);
+// Whether the layer graph's update fits the attention launch's update rows (then the
+// decode step runs it there, under the K/V stream).
+bool layer_update_in_attention_fits(const Problem &p, int n_cand);
 // The layer graph's merge with the step's layer update in extra workgroups (one per
-// sequence; each advances its seq_len).
+// sequence; each advances its seq_len), when it does not fit the attention launch.
 hipError_t launch_attn_merge_layer_update(const Problem &p, int idx_stride, float *out,
                                          const float *partials, const void *k_new,
                                          const void *v_new, const int32_t *cand, int n_cand,

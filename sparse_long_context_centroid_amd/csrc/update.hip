@@ -64,7 +64,7 @@ static void launch_layer_update_t(const Problem &p, const void *k_new, const voi
                                   const ckv_kv &kv, int32_t *assigned, int32_t *err, bool bump,
                                   hipStream_t st) {
     hipLaunchKernelGGL((layer_update_kernel<T, D>), dim3(p.B), dim3(kLayerUpdThreads),
-                       layer_update_lds(p.cdim(), M), st, static_cast<const T *>(k_new),
+                       layer_update_lds(p.cdim(), M, p.Hkv), st, static_cast<const T *>(k_new),
                        static_cast<const T *>(v_new), cand, M, gr.centroids, gr.num_comms,
                        gr.comm_start, gr.comm_size, gr.comm_cap, gr.members, p.Cmax, p.Hkv,
                        static_cast<T *>(kv.k), static_cast<T *>(kv.v), kv.page_table,
@@ -74,7 +74,7 @@ static void launch_layer_update_t(const Problem &p, const void *k_new, const voi
 
 bool layer_update_fits(const Problem &p, int n_cand) {
     return p.cdim() <= 4096 && p.Hkv <= kLayerUpdMaxHeads &&
-           layer_update_lds(p.cdim(), n_cand) <= 65536;
+           layer_update_lds(p.cdim(), n_cand, p.Hkv) <= 65536;
 }
 
 hipError_t launch_layer_update(const Problem &p, const void *k_new, const void *v_new,

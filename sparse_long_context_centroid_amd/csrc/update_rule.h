@@ -222,15 +222,22 @@ __device__ __forceinline__ void sequence_update(int b, const T *__restrict__ k_n
 // equal distance); that community's whole row moves to the running mean, and K/V
 // row n is written in every KV head.
 //
-// One workgroup (of at least kLayerUpdThreads threads) per sequence: k_new is widened to fp64 in LDS and the candidates'
-// rows are staged there by the whole workgroup (every load in flight at once);
-// one thread per (candidate, slice) sums that slice, and the first wave's lanes
-// 0..M-1 add their candidate's slices in order.  LDS: E doubles plus M rows of
-// E+4 floats (the host checks the size).
+// One workgroup (of at least kLayerUpdThreads threads) per sequence: k_new (as
+// fp32, exact for both input types) and the candidates' rows are staged in LDS by
+// the whole workgroup (every load in flight at once); one thread per (candidate,
+// slice) sums that slice in fp64, and the first wave's lanes 0..M-1 add their
+// candidate's slices in order.  All of its LDS comes from one buffer of
+// layer_update_lds(E, M, Hkv) bytes (the host checks the size): the slice sums
+// (M*Hkv doubles), the M rows of E+4 floats, k_new (E floats), then M candidate
+// ids and three ints.
 constexpr int kLayerUpdThreads = 256;
 constexpr int kLayerUpdMaxHeads = 32;  // KV heads (slices) per row
-inline size_t layer_update_lds(int E, int M) {
-    return (size_t)E * sizeof(double) + (size_t)M * (E + 4) * sizeof(float);
+__host__ __device__ constexpr size_t layer_update_part_bytes(int M, int Hkv) {
+    return ((size_t)M * Hkv * sizeof(double) + 15) / 16 * 16;
+}
+inline size_t layer_update_lds(int E, int M, int Hkv) {
+    return layer_update_part_bytes(M, Hkv) + (size_t)M * (E + 4) * sizeof(float) +
+           (size_t)E * sizeof(float) + (size_t)(M + 3) * sizeof(int);
 }
 
 template <typename T, int D>
@@ -244,21 +251,21 @@ __device__ __forceinline__ void layer_update_seq(
     int32_t *__restrict__ seq_len, int bump, int32_t *__restrict__ assigned,
     int32_t *__restrict__ err, unsigned char *__restrict__ s_raw) {
 #pragma clang fp contract(off)
-    __shared__ int s_best, s_slot, s_new;
-    __shared__ int s_cl[CKV_MAX_CAND];
-    __shared__ double s_part[CKV_MAX_CAND * kLayerUpdMaxHeads];
     const int tid = threadIdx.x;
     // threads past the first kLayerUpdThreads (a larger host workgroup) only join
     // the barriers
     const bool act = tid < kLayerUpdThreads;
     const int E = Hkv * D, E4 = E / 4, CS = E + 4;
-    double *kn64 = reinterpret_cast<double *>(s_raw);
-    float *lc = reinterpret_cast<float *>(kn64 + E);
+    double *s_part = reinterpret_cast<double *>(s_raw);
+    float *lc = reinterpret_cast<float *>(s_raw + layer_update_part_bytes(M, Hkv));
+    float *knf = lc + (size_t)M * CS;
+    int *s_cl = reinterpret_cast<int *>(knf + E);
+    int &s_best = s_cl[M], &s_slot = s_cl[M + 1], &s_new = s_cl[M + 2];
     const int n = seq_len[b];
     const int C = min(num_comms[b], Cmax);
     const T *kn = k_new + (size_t)b * E;
     const T *vn = v_new + (size_t)b * E;
-    // round 1: the candidate ids (to LDS) and k_new (widened to fp64)
+    // round 1: the candidate ids and k_new (as fp32) to LDS
     if (tid < M) {
         const int cc = cand[(size_t)b * M + tid];
         s_cl[tid] = (cc >= 0 && cc < C) ? cc : -1;
@@ -273,7 +280,7 @@ __device__ __forceinline__ void layer_update_seq(
 #pragma unroll
         for (int r = 0; r < kMaxPer; ++r)
             if (tid + r * kLayerUpdThreads < E)
-                kn64[tid + r * kLayerUpdThreads] = (double)to_f32(kv[r]);
+                knf[tid + r * kLayerUpdThreads] = to_f32(kv[r]);
     }
     __syncthreads();
     // round 2: the candidates' rows, element 4*k4 .. +3 of community c at float4
@@ -302,14 +309,14 @@ __device__ __forceinline__ void layer_update_seq(
     for (int pr = tid; act && pr < M * Hkv; pr += kLayerUpdThreads) {
         const int sl = pr / Hkv, kh = pr % Hkv;
         const float4 *mu4 = reinterpret_cast<const float4 *>(lc + sl * CS + kh * D);
-        const double2 *k2 = reinterpret_cast<const double2 *>(kn64 + kh * D);
+        const float4 *k4 = reinterpret_cast<const float4 *>(knf + kh * D);
         double s = 0.0;
 #pragma unroll 8
         for (int i4 = 0; i4 < D / 4; ++i4) {
             const float4 m = mu4[i4];
-            const double2 ka = k2[2 * i4], kb = k2[2 * i4 + 1];
-            const double d0 = ka.x - (double)m.x, d1 = ka.y - (double)m.y;
-            const double d2 = kb.x - (double)m.z, d3 = kb.y - (double)m.w;
+            const float4 k = k4[i4];
+            const double d0 = (double)k.x - (double)m.x, d1 = (double)k.y - (double)m.y;
+            const double d2 = (double)k.z - (double)m.z, d3 = (double)k.w - (double)m.w;
             const double q0 = d0 * d0, q1 = d1 * d1, q2 = d2 * d2, q3 = d3 * d3;
             s = s + q0;
             s = s + q1;
@@ -368,7 +375,7 @@ __device__ __forceinline__ void layer_update_seq(
         const float *mu = lc + s_slot * CS;
         for (int i = tid; act && i < E; i += kLayerUpdThreads) {
             const double m0 = (double)mu[i];
-            const double step = (kn64[i] - m0) / cnt;
+            const double step = ((double)knf[i] - m0) / cnt;
             cent[(((size_t)b * E4 + i / 4) * Cmax + best) * 4 + i % 4] = (float)(m0 + step);
         }
     }

@@ -183,7 +183,7 @@ def test_layer_graph_dims(lib):
     fake = C.c_void_p(0x1000)
     g = Bd.ckv_graphs(fake, fake, fake, fake, fake, fake)
     kv = Bd.ckv_kv(fake, fake, fake, 16, 8, 8, fake)
-    # 8 KV heads x d 128: 16 candidate rows of 1028 floats + 1024 doubles > 64 KiB
+    # 8 KV heads x d 128: 16 candidate rows of 1028 floats + 1024 floats > 64 KiB
     assert lib.ckv_local_update(C.byref(lay), fake, fake, fake, 16, C.byref(g), C.byref(kv),
                                 fake, fake, None) == -2
     assert lib.ckv_decode_step(C.byref(lay), fake, fake, fake, C.byref(g), C.byref(kv), fake, 16,

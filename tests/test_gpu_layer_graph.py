@@ -70,6 +70,19 @@ def test_layer_graph_parity_shapes(spec, fused):
     run_parity(I.make_workload(spec, device="cuda"), fused=fused)
 
 
+@pytest.mark.parametrize("n_cand", [8, 12], ids=["update-in-attention", "update-in-merge"])
+def test_layer_graph_update_host_launch(n_cand):
+    """8 KV heads x d 128: with 8 candidates the layer update's staging fits the
+    attention launch's update rows and runs there; with 12 it does not, and the
+    merge launch runs it (each sequence advancing its own seq_len)."""
+    _case(f"layer graph update host, n_cand={n_cand}")
+    spec = I.ConfigSpec("layer-host", 3, 32, 8, 128, 3000, False, 300, 3, I.DT_BF16,
+                        n_cand=n_cand, layer_graph=True)
+    wl = I.make_workload(spec, device="cuda")
+    assert wl.M == n_cand and wl.Hkv * wl.d == 1024
+    run_parity(wl, fused=True)
+
+
 def test_layer_graph_ties_and_zero_query():
     _case("layer graph tied centroids, q = 0")
     wl = I.make_workload(_layer(1), device="cuda", context=4096, steps=3)
