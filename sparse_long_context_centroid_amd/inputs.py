@@ -56,6 +56,7 @@ class ConfigSpec:
     layers: int = 1
     shuffled_pages: bool = False
     layer_graph: bool = False     # one graph per layer, shared by all heads
+    mean_comm_size: float = 64.0  # mean of the geometric community sizes
 
 
 def granularity_spec(base: ConfigSpec, mode: str) -> ConfigSpec:
@@ -297,7 +298,7 @@ def _make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G, gpk, page_
                 C = spec.markov_labels
                 lab = markov_labels(rng, N, C)
             else:
-                lab, C = geometric_partition(rng, N)
+                lab, C = geometric_partition(rng, N, spec.mean_comm_size)
             full = np.full(n, -1, np.int32)
             full[min(S, n):] = lab
             for kvh in range(Hkv):
@@ -314,7 +315,7 @@ def _make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G, gpk, page_
                 C = spec.markov_labels
                 lab = markov_labels(rng, N, C)
             else:
-                lab, C = geometric_partition(rng, N)
+                lab, C = geometric_partition(rng, N, spec.mean_comm_size)
             full = np.full(n, -1, np.int32)
             full[min(S, n):] = lab
             base_labels.append(full)

@@ -1,0 +1,114 @@
+"""The fused decode step (ckv_decode_step: the update in extra workgroups of the
+attention launch, seq_len advanced by the merge) against the four separate calls of
+the C ABI on the same state, over graph granularities, dtypes, head dims, sink
+counts, community sizes down to one or two tokens, and a list longer than its
+stride:
+
+* identical index lists, lengths, sets, candidates, assignments, error bits and
+  updated state (centroids bit for bit, sizes, member pools, seq_len); attention
+  outputs equal within float rounding (the two paths run the same attention code in
+  two kernel instances);
+* a list that runs past its stride is flagged (CKV_DEVERR_INDEX_RANGE) and stops at
+  the stride on both paths;
+* the workloads of communities of one to three tokens (hundreds of kept communities,
+  most of an attention piece's tokens in different communities) against the oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_parity import run_parity
+from sparse_long_context_centroid_amd import binding as Bd
+from sparse_long_context_centroid_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    Bd.load()
+
+
+def _spec(name, B, Hq, Hkv, d, ctx, budget, *, dtype=I.DT_BF16, head=False, layer=False,
+          S=4, M=8, mean=64.0, steps=2):
+    return I.ConfigSpec(name, B, Hq, Hkv, d, ctx, head, budget, steps, dtype, num_sinks=S,
+                        n_cand=M, shuffled_pages=True, layer_graph=layer, mean_comm_size=mean)
+
+
+# (spec, contexts, index_stride or None for sinks + budget)
+CASES = [
+    (_spec("group-bf16-d128", 2, 8, 2, 128, 3000, 300), [3000, 1800], None),
+    (_spec("group-bf16-d128-tiny-communities", 2, 8, 2, 128, 6000, 1000, mean=1.5),
+     [6000, 2500], None),
+    (_spec("perhead-bf16-d128-small-communities", 1, 8, 2, 128, 4000, 600, head=True, mean=3.0),
+     [4000], None),
+    (_spec("layer-bf16-d64-tiny-communities", 2, 8, 4, 64, 5000, 800, layer=True, mean=2.0),
+     [5000, 3100], None),
+    (_spec("group-fp32-d64-tiny-communities", 1, 4, 1, 64, 4000, 700, dtype=I.DT_F32, mean=1.5),
+     [4000], None),
+    (_spec("group-fp32-d128", 2, 8, 2, 128, 2500, 400, dtype=I.DT_F32), [2500, 900], None),
+    (_spec("group-bf16-no-sinks", 2, 8, 2, 128, 2000, 250, S=0), [2000, 1500], None),
+    (_spec("group-bf16-context-below-sinks", 3, 8, 2, 128, 1000, 200, S=7), [1000, 5, 3], None),
+    (_spec("group-bf16-budget-zero", 1, 8, 2, 128, 1500, 0), [1500], None),
+    (_spec("group-bf16-list-past-stride", 2, 8, 2, 128, 3000, 600), [3000, 2000], 250),
+]
+
+
+def _state(layer):
+    torch.cuda.synchronize()
+    return {k: getattr(layer, k).detach().cpu().clone() for k in
+            ("scores", "selected", "num_selected", "cand", "index_len", "index_list",
+             "assigned", "out", "centroids", "comm_size", "members", "seq_len", "err")}
+
+
+@pytest.mark.parametrize("spec,contexts,stride", CASES, ids=[c[0].name for c in CASES])
+def test_fused_step_matches_four_calls(spec, contexts, stride):
+    print(f"\n[case] fused step vs four calls: {spec.name} contexts={contexts} "
+          f"stride={stride}", flush=True)
+    wl = I.make_workload(spec, 57_000, device="cuda", contexts=contexts)
+    if stride is None:
+        stride = int(wl.S + int(wl.budget.max()))
+    L = wl.layers[0]
+    # both layers read the same K/V pools: each step appends row n with the same
+    # bytes in both, and attention reads only the rows below n
+    four = Bd.decode_layer_from_workload(wl, 0, index_stride=stride)
+    fused = Bd.decode_layer_from_workload(wl, 0, index_stride=stride)
+    for t in range(wl.steps):
+        q, kn, vn = L.q[t].contiguous(), L.k_new[t].contiguous(), L.v_new[t].contiguous()
+        four.step(q, kn, vn, wl.scale)
+        a = _state(four)
+        fused.step_fused(q, kn, vn, wl.scale)
+        b = _state(fused)
+        for k in a:
+            if k == "out":
+                continue
+            x, y = a[k], b[k]
+            if k == "index_list":
+                for g in range(x.shape[0]):
+                    n = int(a["index_len"][g])
+                    assert torch.equal(x[g, :n], y[g, :n]), f"step {t} graph {g}: index lists"
+                continue
+            if x.dtype == torch.float32:
+                x, y = x.view(torch.int32), y.view(torch.int32)
+            assert torch.equal(x, y), f"step {t}: {k} differs between the two paths"
+        d = (a["out"] - b["out"]).abs().max().item()
+        assert d <= 1e-5, f"step {t}: outputs differ by {d}"
+    if stride < int(wl.S + int(wl.budget.max())):
+        # the list ran past its stride: flagged, stopped at the stride
+        assert int(a["err"].item()) & Bd.DEVERR_INDEX_RANGE
+        assert int(a["index_len"].max().item()) == stride
+    else:
+        assert int(a["err"].item()) == 0
+
+
+@pytest.mark.parametrize("spec,contexts", [(c[0], c[1]) for c in CASES[1:5]],
+                         ids=[c[0].name for c in CASES[1:5]])
+def test_tiny_communities_match_oracle(spec, contexts):
+    """Communities of one to three tokens: hundreds of kept communities per list."""
+    print(f"\n[case] tiny communities vs oracle: {spec.name} contexts={contexts}", flush=True)
+    wl = I.make_workload(spec, 58_000, device="cuda", contexts=contexts)
+    run_parity(wl, fused=True)
