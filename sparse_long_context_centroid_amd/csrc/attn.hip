@@ -927,9 +927,12 @@ __global__ __launch_bounds__(512) void merge_kernel(int Hq, int Hkv, int gpk,
                                                     int max_splits,
                                                     int32_t *__restrict__ seq_len_bump) {
     extern __shared__ float s_w[];
-    if (seq_len_bump && threadIdx.x == 0 && blockIdx.x % (Hkv * gpk) == 0)
-        seq_len_bump[blockIdx.x / (Hkv * gpk)] += 1;
     merge_graph<D, GH>(blockIdx.x, Hq, Hkv, gpk, out, part, max_splits, s_w);
+    // after the merge, as an add that returns nothing: a read of seq_len first would
+    // hold this workgroup's partial loads behind its round trip
+    if (seq_len_bump && threadIdx.x == 0 && blockIdx.x % (Hkv * gpk) == 0)
+        __hip_atomic_fetch_add(seq_len_bump + blockIdx.x / (Hkv * gpk), 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Workgroups of attn_kernel<T, D, GH, MODE> resident on the current device at

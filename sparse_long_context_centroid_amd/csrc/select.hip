@@ -248,6 +248,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         wt[i] = live ? wt[i] : 0;
         sc[i] = live ? sc[i] : 0.f;
         key[i] = live ? max(order_key(sc[i]), 1u) : 0u;
+        // consumed here, where the other loads are waited for: a first use after
+        // the selected-flag stores below would wait for those stores as well (one
+        // in-order counter covers loads and stores)
+        cst[i] = live ? cst[i] : 0;
     }
     if (tid == 0) cand_n = 0;
 
@@ -460,10 +464,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int ns = S < n ? S : n;
     int32_t *out = idx + (size_t)g * idx_stride;
     bool overflow = false;
-    for (int t = tid; t < ns; t += kSelThreads) {
-        if (t < idx_stride) out[t] = t;
-        else overflow = true;
-    }
     // flat copy of the kept member lists: output slot p (0 <= p < total) belongs
     // to the compacted community e with list_off[e] <= p < list_off[e+1].  When the
     // list fits s_src, each wave first expands its share of the communities into a
@@ -525,6 +525,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             if (src[k] >= 0 && o < idx_stride) out[o] = val[k];
             overflow |= src[k] >= 0 && o >= idx_stride;
         }
+    }
+    // the sinks go out last: stored before the copy, they would hold up the copy's
+    // loads behind them (one in-order counter covers loads and stores)
+    for (int t = tid; t < ns; t += kSelThreads) {
+        if (t < idx_stride) out[t] = t;
+        else overflow = true;
     }
     if (overflow) set_err(err, CKV_DEVERR_INDEX_RANGE);
     if (tid == 0) {
