@@ -28,6 +28,7 @@ Prints ONE JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -447,30 +448,45 @@ def measure(spec, args, scrub, *, extras: bool):
     value_bytes = 0
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    # the timed passes keep the host out of the measured spans: garbage collection is
+    # off, and in the cold passes every layer's scrub and step of a decode step are
+    # queued before the host waits, so the GPU never waits for a launch between a
+    # step's events (the events are read, and the list lengths counted, afterwards)
+    gc.collect()
+    gc.disable()
     for t in range(T):
         phase = 0 if t < args.warmup else (1 if t < args.warmup + args.steps else (
             2 if t < args.warmup + 2 * args.steps else (3 if t < T_timed else 4)))
         tot = 0.0
+        queued = []
         for li, (tm, (q, kn, vn)) in enumerate(zip(timers, qkv)):
             if not args.warm and phase in (1, 2):
                 scrub_sum = scrub.sum()               # cold caches, outside the events
             tm.run(q[t], kn[t], vn[t], wl.scale, per_kernel=phase == 2)
             if phase == 4:
                 continue
-            torch.cuda.synchronize()
             if phase == 3:
+                # warm: back to back, the host waits and reads after every step
+                torch.cuda.synchronize()
                 tot += tm.step_ms()
-            elif phase:
-                tot += tm.step_ms()
-                idx_len = tm.layer.index_len.cpu().numpy()
-                by, ab = step_bytes(tm.layer, idx_len, elem)
-                if phase == 1:
-                    value_bytes += sum(by.values())
-                else:
-                    kernel_ms += np.array(tm.times_ms())
-                    for k, v in by.items():
-                        kernel_bytes[k] += v
-                    attn_only_bytes += ab
+                continue
+            if phase:
+                queued.append(tm)
+            else:
+                torch.cuda.synchronize()
+        if queued:
+            torch.cuda.synchronize()
+        for tm in queued:
+            tot += tm.step_ms()
+            idx_len = tm.layer.index_len.cpu().numpy()
+            by, ab = step_bytes(tm.layer, idx_len, elem)
+            if phase == 1:
+                value_bytes += sum(by.values())
+            else:
+                kernel_ms += np.array(tm.times_ms())
+                for k, v in by.items():
+                    kernel_bytes[k] += v
+                attn_only_bytes += ab
         if phase == 1:
             step_ms.append(tot)
         elif phase == 2:
@@ -480,6 +496,7 @@ def measure(spec, args, scrub, *, extras: bool):
         if t == 0 or (t + 1) % 25 == 0:
             log(f"[bench] step {t + 1}/{T}")
     torch.cuda.synchronize()
+    gc.enable()
     wall = time.perf_counter() - wall0
     err = max(int(l.err.item()) for l in layers)
     if err:
