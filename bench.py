@@ -407,13 +407,18 @@ def measure(spec, args, scrub, *, extras: bool):
     """Generate `spec` on the GPU and time its fused decode step.  Passes, in order:
     warmup; K steps bracketed by a pair of events each (value); K steps with the
     per-kernel events (kernel times, roofline); without --warm, up to 20
-    back-to-back steps without the scrub; then the configuration's remaining
-    decode steps, untimed, so that every step the configuration runs is run.
+    back-to-back steps without the scrub, the host reading results after each; up
+    to 20 steps queued back to back without the scrub or any host wait, one pair of
+    events around them all; then the configuration's remaining decode steps,
+    untimed, so that every step the configuration runs is run.
     With `extras`: centroid rebuild, the dense baseline, the granularity sweep and
     the prefill edges as well."""
     dev = "cuda:0"
     KW = 0 if args.warm else min(args.steps, 20)
-    T_timed = args.warmup + 2 * args.steps + KW
+    KQ = min(args.steps, 20)
+    b_warm = args.warmup + 2 * args.steps
+    b_queued = b_warm + KW
+    T_timed = b_queued + KQ
     T = max(T_timed, spec.steps)
     t0 = time.perf_counter()
     wl = I.make_workload(spec, args.seed, device=dev, steps=T,
@@ -452,18 +457,22 @@ def measure(spec, args, scrub, *, extras: bool):
     # off, and in the cold passes every layer's scrub and step of a decode step are
     # queued before the host waits, so the GPU never waits for a launch between a
     # step's events (the events are read, and the list lengths counted, afterwards)
+    queued_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    queued_ms = None
     gc.collect()
     gc.disable()
     for t in range(T):
         phase = 0 if t < args.warmup else (1 if t < args.warmup + args.steps else (
-            2 if t < args.warmup + 2 * args.steps else (3 if t < T_timed else 4)))
+            2 if t < b_warm else (3 if t < b_queued else (5 if t < T_timed else 4))))
         tot = 0.0
         queued = []
+        if phase == 5 and t == b_queued:
+            queued_ev[0].record()
         for li, (tm, (q, kn, vn)) in enumerate(zip(timers, qkv)):
             if not args.warm and phase in (1, 2):
                 scrub_sum = scrub.sum()               # cold caches, outside the events
             tm.run(q[t], kn[t], vn[t], wl.scale, per_kernel=phase == 2)
-            if phase == 4:
+            if phase in (4, 5):
                 continue
             if phase == 3:
                 # warm: back to back, the host waits and reads after every step
@@ -487,6 +496,10 @@ def measure(spec, args, scrub, *, extras: bool):
                 for k, v in by.items():
                     kernel_bytes[k] += v
                 attn_only_bytes += ab
+        if phase == 5 and t == T_timed - 1:
+            queued_ev[1].record()
+            torch.cuda.synchronize()
+            queued_ms = queued_ev[0].elapsed_time(queued_ev[1]) / KQ
         if phase == 1:
             step_ms.append(tot)
         elif phase == 2:
@@ -538,6 +551,12 @@ def measure(spec, args, scrub, *, extras: bool):
                   "protocol": "back-to-back steps, no scrub; the host synchronises and reads "
                               "results after every step, so its launch latency is exposed"}
                  if step_ms_warm else None),
+        "warm_queued": ({"ms_per_step": queued_ms, "tokens_per_s": wl.B / (queued_ms / 1e3),
+                         "steps": KQ,
+                         "protocol": "steps queued back to back with no scrub and no host wait "
+                                     "between them (a decode loop that does not read results "
+                                     "every step); one pair of events around all of them"}
+                        if queued_ms else None),
         "kernels": per_kernel,
         "attn_share_of_attn_update_bytes": attn_only_bytes / kernel_bytes["attn_update"],
         "wall_s_timed_loop": wall,
