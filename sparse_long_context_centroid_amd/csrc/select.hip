@@ -102,10 +102,10 @@ __device__ __forceinline__ void block_max2(float (&v)[2], float *buf) {
     }
 }
 
-// One wavefront: given a 256-bin histogram, find the bin where the weight summed
-// from the top first exceeds `cap`.  out[0] = that bin (-1 when the whole
-// histogram fits), out[1] = weight of the bins above it.
-__device__ __forceinline__ void find_crossing(const int *hist, int cap, int *out) {
+// One wavefront: given a 256-bin histogram, the bin where the weight summed from
+// the top first exceeds `cap` (-1 when the whole histogram fits) and the weight of
+// the bins above it, as wave-uniform values.
+__device__ __forceinline__ int2 find_crossing(const int *hist, int cap) {
     const int lane = threadIdx.x & (kWave - 1);
     int h[4];
     int t = 0;
@@ -115,25 +115,23 @@ __device__ __forceinline__ void find_crossing(const int *hist, int cap, int *out
         t += h[i];
     }
     const int incl = wave_incl_scan(t);
-    const int s = __builtin_amdgcn_readlane(incl, kWave - 1) - incl + t;  // lanes >= this one
     const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
-    if (total <= cap) {
-        if (lane == 0) {
-            out[0] = -1;
-            out[1] = total;
-        }
-        return;
-    }
-    int above = s - t;
+    if (total <= cap) return make_int2(-1, total);
+    // weight of the bins above this lane's four (lanes above hold the higher bins)
+    int above = total - incl;
+    int bin = -1, at = 0;
 #pragma unroll
     for (int i = 3; i >= 0; --i) {
-        const int incl = above + h[i];
-        if (above <= cap && incl > cap) {
-            out[0] = lane * 4 + i;
-            out[1] = above;
-        }
-        above = incl;
+        const int next = above + h[i];
+        const bool here = (above <= cap) & (next > cap);
+        bin = here ? lane * 4 + i : bin;
+        at = here ? above : at;
+        above = next;
     }
+    // exactly one lane holds the crossing: broadcast it
+    const uint64_t m = __ballot(bin >= 0);
+    const int src = m ? (int)__builtin_ctzll(m) : 0;
+    return make_int2(__builtin_amdgcn_readlane(bin, src), __builtin_amdgcn_readlane(at, src));
 }
 
 // Communities inside the crossing bucket that the fast path ranks exactly.
@@ -163,7 +161,9 @@ __device__ __forceinline__ void probes(uint32_t lo, uint32_t hi, uint32_t (&t)[3
     t[2] = lo + (uint32_t)(wdt * 3 / 4);
 }
 
-// Exclusive block scan of two ints; also returns the totals.  Ends with a barrier.
+// Exclusive block scan of two ints; also returns the totals.  With TAIL, ends with a
+// barrier (so that `tmp` may be written again at once).
+template <bool TAIL>
 __device__ __forceinline__ void block_excl_scan2(int a, int b, int &ea, int &eb, int &ta, int &tb,
                                                  int *tmp) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -190,7 +190,7 @@ __device__ __forceinline__ void block_excl_scan2(int a, int b, int &ea, int &eb,
     eb = pb + ib - b;
     ta = sa;
     tb = sb;
-    __syncthreads();
+    if (TAIL) __syncthreads();
 }
 
 template <int IPT>
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __shared__ uint32_t cand_key[CKV_MAX_CAND];
     __shared__ int cand_id[CKV_MAX_CAND];
     __shared__ int cand_n;
-    __shared__ int histA[256], histB[256], cross[4];
+    __shared__ int histA[256], histB[256];
     __shared__ float fred[2 * kSelWaves];
     // pending entries as (key, id, weight, -) so one LDS read fetches an entry
     __shared__ int4 pendA[kPend], pendB[kPend];
@@ -253,7 +253,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         // in-order counter covers loads and stores)
         cst[i] = live ? cst[i] : 0;
     }
-    if (tid == 0) cand_n = 0;
+    // histograms and counters cleared here: the barrier of the range reduction
+    // below orders these writes before the first use
+    for (int t = tid; t < 256; t += kSelThreads) {
+        histA[t] = 0;
+        histB[t] = 0;
+    }
+    if (tid == 0) {
+        cand_n = 0;
+        pendA_n = 0;
+        pendB_n = 0;
+    }
 
     // ---- fast path: one size-weighted histogram over 256 score buckets that are
     // linear in the fp32 score (monotone, so every bucket is a contiguous range of
@@ -282,15 +292,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         const float x = (sc[i] - lo_s) * bscale;
         bk[i] = wt[i] > 0 ? min(255, max(0, (int)x)) : -1;
     }
-    for (int t = tid; t < 256; t += kSelThreads) {
-        histA[t] = 0;
-        histB[t] = 0;
-    }
-    if (tid == 0) {
-        pendA_n = 0;
-        pendB_n = 0;
-    }
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
         if (bk[i] >= 0) {
@@ -299,10 +300,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
     }
     __syncthreads();
-    if (w == 0) find_crossing(histA, Bt, cross);
-    if (w == 1) find_crossing(histB, M, cross + 2);
-    __syncthreads();
-    const int bA = cross[0], aboveA_b = cross[1], bB = cross[2], aboveB_b = cross[3];
+    // every wave finds both crossings itself (no hand-over through LDS and a barrier)
+    const int2 cA = find_crossing(histA, Bt), cB = find_crossing(histB, M);
+    const int bA = cA.x, aboveA_b = cA.y, bB = cB.x, aboveB_b = cB.y;
     int slotA[IPT], slotB[IPT];
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             tieB += (key[i] == TB && TB > 0) ? 1 : 0;
         }
         int exA, exB, totTieA, totTieB;
-        block_excl_scan2(tieA, tieB, exA, exB, totTieA, totTieB, scan_tmp);
+        block_excl_scan2<true>(tieA, tieB, exA, exB, totTieA, totTieB, scan_tmp);
         int remA, remB;
         {
             int v[2] = {aboveA, aboveB};
@@ -430,7 +430,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         lc += selA[i] ? 1 : 0;
     }
     int ea, ec, total, ksel;
-    block_excl_scan2(la, lc, ea, ec, total, ksel, scan_tmp);
+    // (scan_tmp is not written again before the barrier after the lists)
+    block_excl_scan2<false>(la, lc, ea, ec, total, ksel, scan_tmp);
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
         const int c = tid * IPT + i;
@@ -472,9 +473,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     constexpr int kBatch = 4;
     const bool mapped = total <= kSelSrcMax;
     if (mapped) {
-        for (int e = w; e < ksel; e += kSelWaves) {
-            const int off = list_off[e], len = list_off[e + 1] - off, st0 = list_start[e];
-            for (int j = lane; j < len; j += kWave) s_src[off + j] = st0 + j;
+        // four communities per round: their offsets are read together, then written
+        for (int e0 = w; e0 < ksel; e0 += 4 * kSelWaves) {
+            int off[4], len[4], st0[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * kSelWaves;
+                const int ec = min(e, ksel - 1);
+                off[u] = list_off[ec];
+                len[u] = e < ksel ? list_off[ec + 1] - off[u] : 0;
+                st0[u] = list_start[ec];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                for (int j = lane; j < len[u]; j += kWave) s_src[off[u] + j] = st0[u] + j;
         }
         __syncthreads();
     }
