@@ -320,6 +320,13 @@ __global__ __launch_bounds__(256) void attn_kernel(
     const int b = g / (Hkv * gpk);
     const int kvh = (g / gpk) % Hkv;
     const int h0 = kvh * G + (gpk == 1 ? 0 : g % gpk);
+    // bf16: the graph's GH query rows (one 16-byte piece per thread) are requested
+    // first and stored to LDS only after phase A's loads, so that their round trip
+    // runs beside the list's instead of ahead of it
+    static_assert(!kMfma || GH * D / 8 <= 256, "one query piece per thread");
+    uint4 qv = make_uint4(0, 0, 0, 0);
+    if constexpr (kMfma)
+        qv = reinterpret_cast<const uint4 *>(q + ((size_t)b * Hq + h0) * D)[min(tid, GH * D / 8 - 1)];
     const int n = seq_len[b];
     // index list of this graph (one list serves list_div consecutive graphs)
     const int gl = g / list_div;
@@ -353,12 +360,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
     // 16 registers free for loads in flight.
     constexpr int KB = kMfma ? D / 32 : 1;
     const uint4 *s_q = reinterpret_cast<const uint4 *>(s_big + kAttnWaves * 16 * D / 2);
-    if constexpr (kMfma) {
-        for (int t = tid; t < GH * D / 8; t += blockDim.x)
-            reinterpret_cast<uint4 *>(s_big + kAttnWaves * 16 * D / 2)[t] =
-                reinterpret_cast<const uint4 *>(q + ((size_t)b * Hq + h0) * D)[t];
-        // (visible after phase A's barrier)
-    } else {
+    if constexpr (!kMfma) {
 #pragma unroll
         for (int h = 0; h < GH; ++h) {
             const uint4 u =
@@ -408,6 +410,11 @@ __global__ __launch_bounds__(256) void attn_kernel(
         s_row[t] = pg_ok ? ((pg * Hkv + kvh) << log2ps) + (pos & ((1 << log2ps) - 1)) : -1;
         if (in & !pos_ok) set_err(err, CKV_DEVERR_INDEX_RANGE);
         if (pos_ok & !pg_ok) set_err(err, CKV_DEVERR_UNMAPPED_PAGE);
+    }
+    if constexpr (kMfma) {
+        // the query rows, requested at the start (visible after this barrier)
+        if (c0 == t_begin && tid < GH * D / 8)
+            reinterpret_cast<uint4 *>(s_big + kAttnWaves * 16 * D / 2)[tid] = qv;
     }
     __syncthreads();
 
