@@ -239,7 +239,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         const size_t o = (size_t)g * Cmax + c;
         wt[i] = comm_size[o];
         sc[i] = scores[o];
-        cst[i] = comm_start[o];
     }
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
@@ -248,10 +247,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         wt[i] = live ? wt[i] : 0;
         sc[i] = live ? sc[i] : 0.f;
         key[i] = live ? max(order_key(sc[i]), 1u) : 0u;
-        // consumed here, where the other loads are waited for: a first use after
-        // the selected-flag stores below would wait for those stores as well (one
-        // in-order counter covers loads and stores)
-        cst[i] = live ? cst[i] : 0;
     }
     // histograms and counters cleared here: the barrier of the range reduction
     // below orders these writes before the first use
@@ -303,6 +298,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     // every wave finds both crossings itself (no hand-over through LDS and a barrier)
     const int2 cA = find_crossing(histA, Bt), cB = find_crossing(histB, M);
     const int bA = cA.x, aboveA_b = cA.y, bB = cB.x, aboveB_b = cB.y;
+    // member offsets, requested now: only the compaction below needs them
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) cst[i] = comm_start[(size_t)g * Cmax + min(tid * IPT + i, Cmax - 1)];
     int slotA[IPT], slotB[IPT];
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
@@ -432,6 +430,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int ea, ec, total, ksel;
     // (scan_tmp is not written again before the barrier after the lists)
     block_excl_scan2<false>(la, lc, ea, ec, total, ksel, scan_tmp);
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) cst[i] = selA[i] ? cst[i] : 0;  // waited for before any store
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
         const int c = tid * IPT + i;
