@@ -927,24 +927,29 @@ __device__ __forceinline__ void merge_graph(int g, int Hq, int Hkv, int gpk,
 }
 
 // Merge of one head's split partials into out (m* = max m_s, weights
-// 2^(m_s - m*) / sum_s l_s 2^(m_s - m*)): one workgroup of D threads per (graph,
-// head), one output element per thread (many small workgroups: the launch is a
-// single load round trip, and this grid starts and drains sooner than one
-// workgroup per graph).  Every split slot holds a valid (m, l) -- empty splits
-// carry m = -inf -- so all loads are issued at once, without first reading the list
-// length; acc values of weight-0 splits are never used.  With seq_len_bump (fused
-// decode step) the first head of the first graph of every sequence also advances
-// seq_len, after the step's update has been made.
+// 2^(m_s - m*) / sum_s l_s 2^(m_s - m*)): one single-wave workgroup per 64 output
+// elements of a (graph, head), one element per lane (many small workgroups: the
+// launch is a single load round trip, and this grid starts and drains sooner than
+// one workgroup per graph).  With up to 64 splits, lane s derives split s's weight
+// and the FMAs take it by readlane (no LDS, no barrier); more splits go through
+// LDS.  Every split slot holds a valid (m, l) -- empty splits carry m = -inf -- so
+// all loads are issued at once, without first reading the list length; acc values
+// of weight-0 splits are never used.  With seq_len_bump (fused decode step) the
+// first workgroup of every sequence also advances seq_len, after the step's update
+// has been made.
 template <int D, int GH>
-__global__ __launch_bounds__(D) void merge_kernel(int Hq, int Hkv, int gpk,
-                                                  float *__restrict__ out,
-                                                  const float *__restrict__ part, int max_splits,
-                                                  int32_t *__restrict__ seq_len_bump) {
+__global__ __launch_bounds__(kWave) void merge_kernel(int Hq, int Hkv, int gpk,
+                                                      float *__restrict__ out,
+                                                      const float *__restrict__ part,
+                                                      int max_splits,
+                                                      int32_t *__restrict__ seq_len_bump) {
     extern __shared__ float s_w[];
+    static_assert(D % kWave == 0, "whole waves per head");
     constexpr int kBatch = 32;
-    const int g = blockIdx.x / GH, hh = blockIdx.x % GH;
-    const int i = threadIdx.x;
-    const int lane = i & (kWave - 1);
+    constexpr int WPH = D / kWave;  // workgroups per head
+    const int g = blockIdx.x / (GH * WPH), hh = (blockIdx.x / WPH) % GH;
+    const int lane = threadIdx.x;
+    const int i = (blockIdx.x % WPH) * kWave + lane;
     const int G = Hq / Hkv;
     const int b = g / (Hkv * gpk);
     const int kvh = (g / gpk) % Hkv;
@@ -955,55 +960,67 @@ __global__ __launch_bounds__(D) void merge_kernel(int Hq, int Hkv, int gpk,
     float x[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) x[k] = ph[(size_t)min(k, max_splits - 1) * (D + 2) + 2 + i];
-    // the weights: the first wave
-    if (i < kWave) {
-        if (max_splits <= kWave) {
-            // one split per lane: (m, l) fetched once, reduced with DPP
-            float2 ml = make_float2(-__builtin_inff(), 0.f);
-            if (lane < max_splits) ml = *reinterpret_cast<const float2 *>(ph + (size_t)lane * (D + 2));
-            const float mm = wave_max_f(ml.x);
-            const float f = ml.x == -__builtin_inff() ? 0.f : fast_exp2(ml.x - mm);
-            const float ll = wave_sum_f(ml.y * f);
-            const float inv = ll > 0.f ? 1.f / ll : 0.f;
-            if (lane < max_splits) s_w[lane] = f * inv;
-        } else {
-            float mm = -__builtin_inff();
-            for (int s = lane; s < max_splits; s += kWave) mm = fmaxf(mm, ph[(size_t)s * (D + 2)]);
-            mm = wave_max_f(mm);
-            float ll = 0.f;
-            for (int s = lane; s < max_splits; s += kWave) {
-                const float ms = ph[(size_t)s * (D + 2)];
-                const float f = ms == -__builtin_inff() ? 0.f : fast_exp2(ms - mm);
-                s_w[s] = f;
-                ll += ph[(size_t)s * (D + 2) + 1] * f;
-            }
-            ll = wave_sum_f(ll);
-            const float inv = ll > 0.f ? 1.f / ll : 0.f;
-            for (int s = lane; s < max_splits; s += kWave) s_w[s] *= inv;
-        }
-    }
-    __syncthreads();
     float a = 0.f;
-    for (int s0 = 0; s0 < max_splits; s0 += kBatch) {
-        if (s0 > 0) {
+    if (max_splits <= kWave) {
+        // lane s: split s's weight
+        float2 ml = make_float2(-__builtin_inff(), 0.f);
+        if (lane < max_splits) ml = *reinterpret_cast<const float2 *>(ph + (size_t)lane * (D + 2));
+        const float mm = wave_max_f(ml.x);
+        const float f = ml.x == -__builtin_inff() ? 0.f : fast_exp2(ml.x - mm);
+        const float ll = wave_sum_f(ml.y * f);
+        const float wl = ll > 0.f ? f / ll : 0.f;
 #pragma unroll
-            for (int k = 0; k < kBatch; ++k)
-                x[k] = ph[(size_t)min(s0 + k, max_splits - 1) * (D + 2) + 2 + i];
+        for (int s0 = 0; s0 < kWave; s0 += kBatch) {
+            if (s0 >= max_splits) break;
+            if (s0 > 0) {
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k)
+                    x[k] = ph[(size_t)min(s0 + k, max_splits - 1) * (D + 2) + 2 + i];
+            }
+            // weight 0 (an empty split, or a slot past the last) contributes nothing,
+            // whatever its never-written acc holds; selects, no branches
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s0 + k));
+                const bool use = (s0 + k < max_splits) & (wk != 0.f);
+                const float term = x[k] * wk;
+                a += use ? term : 0.f;
+            }
         }
-        // weight 0 (an empty split, or a slot past the last) contributes nothing,
-        // whatever its never-written acc holds; selects, no branches
+    } else {
+        float mm = -__builtin_inff();
+        for (int s = lane; s < max_splits; s += kWave) mm = fmaxf(mm, ph[(size_t)s * (D + 2)]);
+        mm = wave_max_f(mm);
+        float ll = 0.f;
+        for (int s = lane; s < max_splits; s += kWave) {
+            const float ms = ph[(size_t)s * (D + 2)];
+            const float f = ms == -__builtin_inff() ? 0.f : fast_exp2(ms - mm);
+            s_w[s] = f;
+            ll += ph[(size_t)s * (D + 2) + 1] * f;
+        }
+        ll = wave_sum_f(ll);
+        const float inv = ll > 0.f ? 1.f / ll : 0.f;
+        for (int s = lane; s < max_splits; s += kWave) s_w[s] *= inv;
+        __syncthreads();
+        for (int s0 = 0; s0 < max_splits; s0 += kBatch) {
+            if (s0 > 0) {
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            const float wk = s_w[min(s0 + k, max_splits - 1)];
-            const bool use = (s0 + k < max_splits) & (wk != 0.f);
-            const float term = x[k] * wk;
-            a += use ? term : 0.f;
+                for (int k = 0; k < kBatch; ++k)
+                    x[k] = ph[(size_t)min(s0 + k, max_splits - 1) * (D + 2) + 2 + i];
+            }
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const float wk = s_w[min(s0 + k, max_splits - 1)];
+                const bool use = (s0 + k < max_splits) & (wk != 0.f);
+                const float term = x[k] * wk;
+                a += use ? term : 0.f;
+            }
         }
     }
     out[((size_t)b * Hq + h0 + hh) * D + i] = a;
     // after the merge, as an add that returns nothing: a read of seq_len first would
     // hold this workgroup's partial loads behind its round trip
-    if (seq_len_bump && i == 0 && hh == 0 && g % (Hkv * gpk) == 0)
+    if (seq_len_bump && lane == 0 && blockIdx.x % (GH * WPH) == 0 && g % (Hkv * gpk) == 0)
         __hip_atomic_fetch_add(seq_len_bump + g / (Hkv * gpk), 1, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1177,9 +1194,10 @@ static hipError_t launch_merge(const Problem &p, int ms, float *out, const float
     const int GH = p.heads_per_graph();
 #define CKV_MERGE_CASE(DD, HH)                                                                 \
     if (p.D == DD && GH == HH) {                                                               \
-        hipExtLaunchKernelGGL((merge_kernel<DD, HH>), dim3(p.NG() * HH), dim3(DD),             \
-                              (size_t)ms * sizeof(float), st, p.ev_start, p.ev_stop, 0, p.Hq,  \
-                              p.Hkv, p.gpk, out, partials, ms, bump_seq_len);                  \
+        hipExtLaunchKernelGGL((merge_kernel<DD, HH>), dim3(p.NG() * HH * (DD / kWave)),        \
+                              dim3(kWave), (size_t)ms * sizeof(float), st, p.ev_start,         \
+                              p.ev_stop, 0, p.Hq, p.Hkv, p.gpk, out, partials, ms,             \
+                              bump_seq_len);                                                   \
         return hipGetLastError();                                                              \
     }
     CKV_MERGE_CASE(128, 1) CKV_MERGE_CASE(128, 2) CKV_MERGE_CASE(128, 4) CKV_MERGE_CASE(128, 8)
