@@ -167,10 +167,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
 // The centroid of (b, k) is set b*Hkv + k of the interleaved layout.  A workgroup
 // holds one wave per KV head (up to kLayerScoreWaves; more heads loop): each wave
 // runs the lane-per-community stream above on its head's slice with its G queries
-// in its own LDS rows, and the waves' maxima meet in LDS.
+// in its own LDS rows, and the waves' maxima meet in LDS.  A workgroup covers CPW
+// communities: 64, or 32 when the grid would otherwise leave most compute units
+// idle (lanes 32-63 then repeat lanes 0-31: the same addresses in the same load
+// instructions, so no extra bytes, and only lanes 0-31 write).
 constexpr int kLayerScoreWaves = 8;
 
-template <typename T, int D, int GH>
+template <typename T, int D, int GH, int CPW>
 __global__ __launch_bounds__(kLayerScoreWaves * kWave) void layer_score_kernel(
     const T *__restrict__ q, const float *__restrict__ cent, const int32_t *__restrict__ num_comms,
     const int32_t *__restrict__ comm_size, int Cmax, int Hq, int Hkv, double scale,
@@ -186,10 +189,11 @@ __global__ __launch_bounds__(kLayerScoreWaves * kWave) void layer_score_kernel(
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
     const int nw = blockDim.x / kWave;
-    const int c0 = blockIdx.x * kWave + lane;
+    static_assert(CPW == 32 || CPW == 64, "communities per workgroup");
+    const int c0 = blockIdx.x * CPW + (lane & (CPW - 1));
     const int c = min(c0, Cmax - 1);
     const int C = min(num_comms[b], Cmax);
-    if ((int)(blockIdx.x * kWave) >= C) return;
+    if ((int)(blockIdx.x * CPW) >= C) return;
     using Q4 = typename std::conditional<sizeof(T) == 2, uint2, float4>::type;
     double *sqw = sq[w];
     float best = -__builtin_inff();
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(kLayerScoreWaves * kWave) void layer_score_kernel(
     __syncthreads();
     if (w == 0) {
         for (int i = 1; i < nw; ++i) best = s_best[i][lane] > best ? s_best[i][lane] : best;
-        if (c0 < C)
+        if (c0 < C && lane < CPW)
             scores[(size_t)b * Cmax + c] =
                 comm_size[(size_t)b * Cmax + c] > 0 ? best : -__builtin_inff();
     }
@@ -308,8 +312,13 @@ template <typename T, int D, int GH>
 static void launch_layer_score_t(const Problem &p, const void *q, const ckv_graphs &gr,
                                  double scale, float *scores, hipStream_t st) {
     const int nw = p.Hkv < kLayerScoreWaves ? p.Hkv : kLayerScoreWaves;
-    hipExtLaunchKernelGGL((layer_score_kernel<T, D, GH>),
-                          dim3((p.Cmax + kWave - 1) / kWave, p.B), dim3(nw * kWave), 0, st,
+    // narrow workgroups only for a grid of at most a quarter as many workgroups as
+    // compute units (1 x 32K: 9 -> 18 workgroups, 9.0 -> 7.5 us); at 4 x 128K (132
+    // workgroups) the repeated lanes' requests made it slower (10.4 -> 13.0 us)
+    const bool narrow = 4LL * ((p.Cmax + kWave - 1) / kWave) * p.B <= device_cu_count();
+    auto kernel = narrow ? layer_score_kernel<T, D, GH, 32> : layer_score_kernel<T, D, GH, 64>;
+    const int cpw = narrow ? 32 : 64;
+    hipExtLaunchKernelGGL(kernel, dim3((p.Cmax + cpw - 1) / cpw, p.B), dim3(nw * kWave), 0, st,
                           p.ev_start, p.ev_stop, 0,
                           static_cast<const T *>(q), gr.centroids, gr.num_comms, gr.comm_size,
                           p.Cmax, p.Hq, p.Hkv, scale, scores);
