@@ -30,13 +30,18 @@ constexpr int kUpdLdsFloats(int D) { return 2 * D + CKV_MAX_CAND * kUpdCentStrid
 
 // One wavefront updates graph g.  cand[0..M) are community ids (-1 = none);
 // C communities are in use.  lds_row holds kUpdLdsFloats(D) floats of LDS private
-// to this wave.  When write_kv, the wave also stores k_new / v_new into K/V row
-// `kv_row` (element offset), or flags an unmapped page.
+// to this wave.  When write_kv, the wave also stores k_new / v_new into K/V row n
+// of KV head kvh (seq_pages: the sequence's page-table row), or flags an unmapped
+// page.
 //
 // Every global read is issued before any is waited for, in two dependent rounds:
-// the candidate ids, then all candidates' centroids (4 lanes per candidate) with
-// their sizes, capacities and starts.  The centroids are parked in LDS; the lane
-// that owns a candidate then sums its distance there, in element order.
+// the candidate ids (beside the caller's seq_len and community-count loads), then
+// all candidates' centroids (4 lanes per candidate) with their sizes, capacities
+// and starts, and the page-table entry of row n.  The page-table load is issued
+// after the candidate ids and unconditionally (clamped slot, validity by selects),
+// so that waiting for the ids never waits for it.  The centroids are parked in
+// LDS; the lane that owns a candidate then sums its distance there, in element
+// order.
 template <typename T, int D>
 __device__ __forceinline__ void local_update_wave(const T *__restrict__ kn, const T *__restrict__ vn,
                                   const int *cand, int M, int C, size_t g, int Cmax,
@@ -44,8 +49,10 @@ __device__ __forceinline__ void local_update_wave(const T *__restrict__ kn, cons
                                   int32_t *__restrict__ comm_size,
                                   const int32_t *__restrict__ comm_cap,
                                   int32_t *__restrict__ members, int n, bool write_kv,
-                                  T *__restrict__ kc, T *__restrict__ vc, size_t kv_row,
-                                  bool kv_ok, int32_t *__restrict__ assigned,
+                                  T *__restrict__ kc, T *__restrict__ vc,
+                                  const int32_t *__restrict__ seq_pages, int log2ps,
+                                  int max_pages, int num_pages, int kvh, int Hkv,
+                                  int32_t *__restrict__ assigned,
                                   int32_t *__restrict__ err, float *lds_row) {
 #pragma clang fp contract(off)
     constexpr int LPC = kUpdLanesPerCand;
@@ -61,6 +68,9 @@ __device__ __forceinline__ void local_update_wave(const T *__restrict__ kn, cons
     T knr[D / kWave > 0 ? D / kWave : 1];
 #pragma unroll
     for (int r = 0; r < D / kWave; ++r) knr[r] = kn[lane + r * kWave];
+    // K/V row n: its page-table entry, requested behind the ids
+    const int lp = n >> log2ps;
+    const int pg = seq_pages[min(lp, max_pages - 1)];
     const int c = (slot < M && cc >= 0 && cc < C) ? cc : -1;
     const int cl = c >= 0 ? c : 0;  // loads below are unconditional
     // round 2: the centroid share, size, capacity and start of the candidate
@@ -136,6 +146,9 @@ __device__ __forceinline__ void local_update_wave(const T *__restrict__ kn, cons
         }
     }
     if (write_kv) {
+        const bool kv_ok = lp < max_pages && pg >= 0 && pg < num_pages;
+        const size_t kv_row =
+            kv_ok ? ((((size_t)pg * Hkv + kvh) << log2ps) + (n & ((1 << log2ps) - 1))) * D : 0;
         if (kv_ok) {
             for (int i = lane; i < D; i += kWave) {
                 kc[kv_row + i] = kn[i];
@@ -174,14 +187,10 @@ __device__ __forceinline__ void graph_update(size_t g, const T *__restrict__ k_n
     const T *kn = k_new + ((size_t)b * Hkv + kvh) * D;
     const T *vn = v_new + ((size_t)b * Hkv + kvh) * D;
     const int C = min(num_comms[g], Cmax);
-    const int lp = n >> log2ps;
-    const int pg = lp < max_pages ? page_table[(size_t)b * max_pages + lp] : -1;
-    const bool ok = pg >= 0 && pg < num_pages;
-    const size_t row =
-        ok ? ((((size_t)pg * Hkv + kvh) << log2ps) + (n & ((1 << log2ps) - 1))) * D : 0;
     local_update_wave<T, D>(kn, vn, cand + g * M, M, C, g, Cmax, cent, comm_start, comm_size,
-                            comm_cap, members, n, gl % gpk == 0, kc, vc, row, ok, assigned, err,
-                            lds_row);
+                            comm_cap, members, n, gl % gpk == 0, kc, vc,
+                            page_table + (size_t)b * max_pages, log2ps, max_pages, num_pages, kvh,
+                            Hkv, assigned, err, lds_row);
 }
 
 // All graphs of sequence b, one wavefront per graph (looping when the workgroup
