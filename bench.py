@@ -86,6 +86,7 @@ KERNELS = ["score", "select", "attn_update", "merge"]
 PMC_FILES = {
     "qwen3-8b-layer-b4-ctx128k-group": "attn_kernel_b4_ctx128k_pmc_traffic.txt",
     "qwen3-8b-36layer-ragged16-ctx8k-128k-paged": "attn_kernel_ragged16_36layer_pmc_traffic.txt",
+    "qwen3-8b-layer-b4-ctx128k-perhead": "attn_kernel_b4_ctx128k_perhead_pmc_traffic.txt",
 }
 ATTN_SOURCES = ["attn.hip", "update_rule.h", "ckv_device.h", "ckv_internal.h"]
 
