@@ -404,6 +404,39 @@ def update_cost_vs_context(args, scrub, contexts=(8192, 131072), steps=24):
     return out
 
 
+def four_call_step(args, scrub, steps=24):
+    """One decode step of the 4 x 128K workload through the four separate C-ABI
+    calls (ckv_score_centroids, ckv_select, ckv_sparse_decode_attn, ckv_local_update:
+    5 launches, the update after the attention instead of inside its launch), beside
+    the fused ckv_decode_step on the same state.  Cold protocol: a scrub before each
+    step, one pair of events around the calls."""
+    wl = I.make_workload(3, args.seed, device="cuda:0", steps=2 * steps, layers=1)
+    lay = build_layers(wl, int(wl.S + wl.budget.max()))[0]
+    L = wl.layers[0]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    res = {}
+    for name, fn, base in (("four_calls", lay.step, 0), ("fused", lay.step_fused, steps)):
+        us = []
+        for t in range(base, base + steps):
+            if not args.warm:
+                scrub_sum = scrub.sum()
+            ev[0].record()
+            fn(L.q[t], L.k_new[t], L.v_new[t], wl.scale)
+            ev[1].record()
+            torch.cuda.synchronize()
+            if t - base >= 4:
+                us.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        res[name] = dict(us_median=float(np.median(us)), us_mean=float(np.mean(us)),
+                         steps=len(us))
+    if int(lay.err.item()):
+        raise SystemExit("device error flag during the four-call timing")
+    del lay, wl, L
+    torch.cuda.empty_cache()
+    res["what"] = ("one 4 x 128K decode step: the four C-ABI calls in turn against "
+                   "ckv_decode_step, each after a cache scrub, events around the calls")
+    return res
+
+
 def measure(spec, args, scrub, *, extras: bool):
     """Generate `spec` on the GPU and time its fused decode step.  Passes, in order:
     warmup; K steps bracketed by a pair of events each (value); K steps with the
@@ -657,6 +690,10 @@ def main():
         u = res["update_cost_vs_context"]
         log(f"[bench] local update alone: {u['8192']['us_median']:.2f} us at 8K, "
             f"{u['131072']['us_median']:.2f} us at 128K")
+        if args.config == 3:
+            res["four_call_step"] = f4 = four_call_step(args, scrub)
+            log(f"[bench] four C-ABI calls {f4['four_calls']['us_median']:.2f} us per step, "
+                f"fused {f4['fused']['us_median']:.2f} us")
     if not args.no_granularity:
         res["granularity_sweep"] = granularity_sweep(spec, args, scrub, 2 if spec.dtype == I.DT_BF16 else 4)
     if args.config != 4 and not args.no_config4:

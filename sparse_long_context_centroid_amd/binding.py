@@ -358,11 +358,32 @@ class DecodeLayer:
         self.update(k_new, v_new)
 
     def step_fused(self, q, k_new, v_new, scale, events=None):
-        """The same step through ckv_decode_step (4 launches; 5 for the layer graph)."""
-        ckv_decode_step(self.dims, q, k_new, v_new, self.graphs, self.kv, self.budget, self.M,
-                        scale, self.scores, self.index_list, self.index_len, self.num_selected,
-                        self.cand, self.selected, self.assigned, self.out, self.ws, self.err,
-                        events=events)
+        """The same step through ckv_decode_step (4 launches; 5 for the layer graph).
+        Without events the layer's own arguments are marshalled once and reused
+        while the same objects stay in place, so a call converts only q, k_new,
+        v_new, the scale and the stream."""
+        if events is not None:
+            ckv_decode_step(self.dims, q, k_new, v_new, self.graphs, self.kv, self.budget,
+                            self.M, scale, self.scores, self.index_list, self.index_len,
+                            self.num_selected, self.cand, self.selected, self.assigned, self.out,
+                            self.ws, self.err, events=events)
+            return
+        own = (self.dims, self.graphs, self.kv, self.budget, self.scores, self.index_list,
+               self.index_len, self.num_selected, self.cand, self.selected, self.assigned,
+               self.out, self.ws, self.err)
+        key = tuple(map(id, own)) + (self.M,)
+        cached = getattr(self, "_fused_args", None)
+        if cached is None or cached[0] != key:
+            head = (C.byref(self.dims),)
+            mid = (C.byref(self.graphs), C.byref(self.kv), _ptr(self.budget), self.M)
+            tail = (_ptr(self.scores), _ptr(self.index_list), self.index_list.shape[1],
+                    _ptr(self.index_len), _ptr(self.num_selected), _ptr(self.cand),
+                    _ptr(self.selected), _ptr(self.assigned), _ptr(self.out), _ptr(self.ws),
+                    self.ws.numel() * self.ws.element_size(), _ptr(self.err), None)
+            cached = self._fused_args = (key, own, head, mid, tail)
+        _, _, head, mid, tail = cached
+        _check(load().ckv_decode_step(*head, _ptr(q), _ptr(k_new), _ptr(v_new), *mid, scale,
+                                      *tail, _stream(None)), "ckv_decode_step")
 
     def step_noalloc(self, q, k_new, v_new, scale, events=None):
         """The same step through ckv_decode_step_noalloc (no workspace argument)."""

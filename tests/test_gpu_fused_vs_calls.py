@@ -112,3 +112,47 @@ def test_tiny_communities_match_oracle(spec, contexts):
     print(f"\n[case] tiny communities vs oracle: {spec.name} contexts={contexts}", flush=True)
     wl = I.make_workload(spec, 58_000, device="cuda", contexts=contexts)
     run_parity(wl, fused=True)
+
+
+def test_fused_step_follows_replaced_buffers():
+    """step_fused marshals the layer's own buffers once and reuses them while the
+    same objects stay in place: after buffers are replaced, the next step writes
+    into the new ones (and leaves the old ones as they were), equal to a layer whose
+    every step marshals its arguments afresh (the path with timing events)."""
+    spec = _spec("group-bf16-d128-rebound", 2, 8, 2, 128, 3000, 300, steps=3)
+    print(f"\n[case] fused step after replaced buffers: {spec.name}", flush=True)
+    wl = I.make_workload(spec, 57_100, device="cuda", contexts=[3000, 1700])
+    L = wl.layers[0]
+    cached = Bd.decode_layer_from_workload(wl, 0)
+    fresh = Bd.decode_layer_from_workload(wl, 0)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    for t in range(wl.steps):
+        q, kn, vn = L.q[t].contiguous(), L.k_new[t].contiguous(), L.v_new[t].contiguous()
+        old = None
+        if t > 0:
+            old = {k: getattr(cached, k) for k in ("out", "index_list", "cand", "assigned")}
+            snap = {k: v.detach().clone() for k, v in old.items()}
+            cached.out = torch.full_like(cached.out, float("nan"))
+            cached.index_list = torch.full_like(cached.index_list, -7)
+            cached.cand = torch.full_like(cached.cand, -7)
+            cached.assigned = torch.full_like(cached.assigned, -7)
+        cached.step_fused(q, kn, vn, wl.scale)
+        fresh.step_fused(q, kn, vn, wl.scale, events=ev)
+        a, b = _state(cached), _state(fresh)
+        for k in a:
+            if k == "out":
+                continue
+            x, y = a[k], b[k]
+            if k == "index_list":
+                for g in range(x.shape[0]):
+                    n = int(b["index_len"][g])
+                    assert torch.equal(x[g, :n], y[g, :n]), f"step {t} graph {g}: index lists"
+                continue
+            if x.dtype == torch.float32:
+                x, y = x.view(torch.int32), y.view(torch.int32)
+            assert torch.equal(x, y), f"step {t}: {k} differs"
+        assert torch.equal(a["out"], b["out"]), f"step {t}: outputs differ"
+        if old is not None:
+            for k, v in old.items():
+                assert torch.equal(v.cpu(), snap[k].cpu()), f"step {t}: the replaced {k} was written"
+    assert int(b["err"].item()) == 0
