@@ -95,7 +95,7 @@ class Layer:
     comm_size: np.ndarray         # [NG, Cmax] int32
     comm_cap: np.ndarray          # [NG, Cmax] int32
     members: np.ndarray           # [pool] int32 token positions (-1 = free slot)
-    k_pages: torch.Tensor         # [num_pages, Hkv, PAGE_SIZE, d]
+    k_pages: torch.Tensor         # [num_pages, Hkv, page_size, d]
     v_pages: torch.Tensor
     base_labels: List[np.ndarray]  # per (b, kvh): label of every position (-1 = sink)
     centres: List[np.ndarray]      # per (b, kvh): [C, d] fp32 generating centres
@@ -198,9 +198,11 @@ def make_workload(cfg: int | ConfigSpec, seed: Optional[int] = None, *, device: 
                   context: Optional[int] = None, batch: Optional[int] = None,
                   steps: Optional[int] = None, layers: Optional[int] = None,
                   budget: Optional[int] = None, contexts: Optional[List[int]] = None,
-                  n_cand: Optional[int] = None, slack: Optional[int] = None) -> Workload:
+                  n_cand: Optional[int] = None, slack: Optional[int] = None,
+                  page_size: Optional[int] = None) -> Workload:
     """Build a seeded workload.  Overrides shrink a configuration for tests while
-    keeping its structure (same recipe, fewer tokens/sequences/steps)."""
+    keeping its structure (same recipe, fewer tokens/sequences/steps); page_size
+    (a power of two, default PAGE_SIZE) sets the tokens per page of the KV pools."""
     spec = CONFIGS[cfg] if isinstance(cfg, int) else cfg
     cfg_id = CONFIGS.index(spec) if spec in CONFIGS else 99
     if seed is None:
@@ -233,7 +235,9 @@ def make_workload(cfg: int | ConfigSpec, seed: Optional[int] = None, *, device: 
     else:
         bud = np.full(B, spec.budget, np.int64)
 
-    ps = PAGE_SIZE
+    ps = PAGE_SIZE if page_size is None else int(page_size)
+    if ps < 1 or ps & (ps - 1):
+        raise ValueError(f"page_size {ps} is not a power of two")
     pages_per_seq = [(int(n) + T + ps - 1) // ps for n in ns]
     max_pages = max(pages_per_seq)
     num_pages = int(sum(pages_per_seq))
@@ -251,7 +255,7 @@ def make_workload(cfg: int | ConfigSpec, seed: Optional[int] = None, *, device: 
     layer_objs = []
     for li in range(L):
         layer_objs.append(_make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G,
-                                      gpk, page_table, num_pages, tdt, device))
+                                      gpk, page_table, num_pages, tdt, device, ps))
     # one community stride for every layer: pad each layer's per-community arrays
     # to the largest (padding columns are empty communities past num_comms)
     Cmax = max(lo.centroids.shape[1] for lo in layer_objs)
@@ -280,7 +284,7 @@ def _pad_communities(layer: Layer, Cmax: int) -> None:
 
 
 def _make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G, gpk, page_table,
-                num_pages, tdt, device) -> Layer:
+                num_pages, tdt, device, ps=PAGE_SIZE) -> Layer:
     layer = gpk == 0
     NG = B if layer else B * Hkv * gpk
     gps = 1 if layer else Hkv * gpk           # graphs per sequence
@@ -359,16 +363,16 @@ def _make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G, gpk, page_
     members = np.concatenate(pools) if pools else np.zeros(0, np.int32)
 
     # --- bulk keys / values on the device, written into the paged pool ----------
-    k_pages = torch.zeros((num_pages, Hkv, PAGE_SIZE, d), dtype=tdt, device=device)
+    k_pages = torch.zeros((num_pages, Hkv, ps, d), dtype=tdt, device=device)
     v_pages = torch.zeros_like(k_pages)
     centroids = torch.zeros((NG, Cmax, cd), dtype=torch.float32, device=device)
     for b in range(B):
         n = int(ns[b])
-        npg = (n + PAGE_SIZE - 1) // PAGE_SIZE
+        npg = (n + ps - 1) // ps
         pt = torch.from_numpy(page_table[b, :npg].astype(np.int64)).to(device)
         gk = _torch_gen(device, seed, 3, li, b)
-        kl = torch.empty((Hkv, npg * PAGE_SIZE, d), dtype=torch.float32, device=device)
-        vl = torch.randn((Hkv, npg * PAGE_SIZE, d), generator=gk, device=device)
+        kl = torch.empty((Hkv, npg * ps, d), dtype=torch.float32, device=device)
+        vl = torch.randn((Hkv, npg * ps, d), generator=gk, device=device)
         for kvh in range(Hkv):
             lab = torch.from_numpy(base_labels[b * Hkv + kvh].astype(np.int64)).to(device)
             cen = torch.from_numpy(centres[b * Hkv + kvh]).to(device)
@@ -381,8 +385,8 @@ def _make_layer(spec, seed, li, B, ns, T, slack, S, M, d, Hq, Hkv, G, gpk, page_
         kb = kl.to(tdt)
         vb = vl.to(tdt)
         # logical [Hkv, pos, d] -> physical pages [page, Hkv, slot, d]
-        k_pages[pt] = kb.view(Hkv, npg, PAGE_SIZE, d).permute(1, 0, 2, 3)
-        v_pages[pt] = vb.view(Hkv, npg, PAGE_SIZE, d).permute(1, 0, 2, 3)
+        k_pages[pt] = kb.view(Hkv, npg, ps, d).permute(1, 0, 2, 3)
+        v_pages[pt] = vb.view(Hkv, npg, ps, d).permute(1, 0, 2, 3)
         # initial centroids: fp64 mean of the stored member keys, rounded to fp32
         for kvh in range(Hkv):
             k64 = kb[kvh, :n].to(torch.float64)

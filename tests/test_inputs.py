@@ -38,11 +38,15 @@ def test_layers_share_stride_and_members_are_own_positions(cfg, kw):
         assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
 
 
-def test_logical_kv_gather_matches_the_page_walk():
+@pytest.mark.parametrize("ps", [None, 1, 4, 256])
+def test_logical_kv_gather_matches_the_page_walk(ps):
     """The test-side gather of the paged pools into token order equals a plain walk
-    over the page table (unmapped pages stay zero)."""
+    over the page table (unmapped pages stay zero), at the default and other page
+    sizes."""
     import helpers as H
-    wl = I.make_workload(4, contexts=[700, 1600, 33], steps=2, layers=1)
+    wl = I.make_workload(4, contexts=[700, 1600, 33], steps=2, layers=1, page_size=ps)
+    assert wl.page_size == (I.PAGE_SIZE if ps is None else ps)
+    assert tuple(wl.layers[0].k_pages.shape[1:]) == (wl.Hkv, wl.page_size, wl.d)
     L = wl.layers[0]
     K, V = H.logical_kv(wl, L)
     pt = wl.page_table.cpu().numpy()
@@ -58,3 +62,8 @@ def test_logical_kv_gather_matches_the_page_walk():
                 V2[b, :, p * ps:(p + 1) * ps] = vp[pt[b, p]]
     assert (pt < 0).any()
     assert np.array_equal(K, K2) and np.array_equal(V, V2)
+
+
+def test_page_size_must_be_a_power_of_two():
+    with pytest.raises(ValueError):
+        I.make_workload(0, page_size=48)
