@@ -156,3 +156,41 @@ def test_fused_step_follows_replaced_buffers():
             for k, v in old.items():
                 assert torch.equal(v.cpu(), snap[k].cpu()), f"step {t}: the replaced {k} was written"
     assert int(b["err"].item()) == 0
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused-step", "four-calls"])
+def test_step_on_a_side_stream(fused):
+    """Every launch of a call goes to the stream it is given: the same steps on a
+    second stream (torch's current stream inside the block; default priority) give
+    the state and outputs of the default stream bit for bit."""
+    spec = _spec("group-bf16-d128-stream", 2, 8, 2, 128, 3000, 300, steps=3)
+    print(f"\n[case] side stream: {spec.name} fused={fused}", flush=True)
+    wl = I.make_workload(spec, 57_200, device="cuda", contexts=[3000, 2200])
+    L = wl.layers[0]
+    main = Bd.decode_layer_from_workload(wl, 0)
+    side = Bd.decode_layer_from_workload(wl, 0)
+    # the two layers own separate K/V pools: each appends its own rows
+    side.k, side.v = side.k.clone(), side.v.clone()
+    side.kv = Bd.make_kv(side.k, side.v, side.page_table, wl.page_size, side.seq_len)
+    s = torch.cuda.Stream()
+    for t in range(wl.steps):
+        q, kn, vn = L.q[t].contiguous(), L.k_new[t].contiguous(), L.v_new[t].contiguous()
+        torch.cuda.synchronize()
+        (main.step_fused if fused else main.step)(q, kn, vn, wl.scale)
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            (side.step_fused if fused else side.step)(q, kn, vn, wl.scale)
+        torch.cuda.synchronize()
+        a, b = _state(main), _state(side)
+        for k in a:
+            x, y = a[k], b[k]
+            if k == "index_list":
+                for g in range(x.shape[0]):
+                    n = int(a["index_len"][g])
+                    assert torch.equal(x[g, :n], y[g, :n]), f"step {t} graph {g}: index lists"
+                continue
+            if x.dtype == torch.float32:
+                x, y = x.view(torch.int32), y.view(torch.int32)
+            assert torch.equal(x, y), f"step {t}: {k} differs between the streams"
+    assert int(a["err"].item()) == 0
+    assert torch.equal(main.k, side.k) and torch.equal(main.v, side.v)
