@@ -132,6 +132,48 @@ def test_unmapped_page_is_flagged_and_skipped():
         assert np.max(np.abs(out[0, h] - ref.astype(np.float64))) < 2e-3
 
 
+def test_out_of_range_entries_are_flagged_and_skipped():
+    """Index-list entries outside [0, seq_len) given to the attention call (negative,
+    at n, past n, far past the cache) are skipped and flagged; the output is the
+    oracle's attention over the list's valid entries, on lists long enough to span
+    several attention workgroups, with bad entries at both ends of the lists."""
+    import oracle.ckv_oracle as O
+    _case("out-of-range index entries")
+    wl = I.make_workload(4, device="cuda", contexts=[3000, 1200], steps=1, layers=1)
+    stride = 1024
+    layer = Bd.decode_layer_from_workload(wl, 0, index_stride=stride)
+    rng = np.random.default_rng(11)
+    lists, lens, valid = np.zeros((layer.NG, stride), np.int32), np.zeros(layer.NG, np.int32), []
+    for g in range(layer.NG):
+        n = int(wl.seq_len0[g // wl.Hkv])
+        m = 700 + 17 * g
+        good = rng.choice(n, m - 6, replace=False).astype(np.int32)
+        bad = np.array([-1, n, n + 5, -7, 1 << 30, n + 1000], np.int32)
+        lst = np.concatenate([bad[:1], good, bad[1:]])
+        lst[[191, 192, 383]] = bad[[1, 2, 3]]          # inside and between pieces
+        lists[g, :m] = lst
+        lens[g] = m
+        valid.append(lst[(lst >= 0) & (lst < n)])
+    layer.index_list.copy_(torch.from_numpy(lists))
+    layer.index_len.copy_(torch.from_numpy(lens))
+    L = wl.layers[0]
+    q = L.q[0].contiguous()
+    layer.attend(q, wl.scale)
+    torch.cuda.synchronize()
+    assert int(layer.err.item()) & Bd.DEVERR_INDEX_RANGE
+    out = layer.out.cpu().numpy().astype(np.float64)
+    K, V = H.logical_kv(wl, L)
+    qn = H.raw_np(q)
+    G = wl.Hq // wl.Hkv
+    for b in range(wl.B):
+        for h in range(wl.Hq):
+            g = b * wl.Hkv + h // G
+            ref = O.attend(qn[b, h], K[b, h // G], V[b, h // G], valid[g], wl.scale)
+            err = np.abs(out[b, h] - ref)
+            rel = np.linalg.norm(out[b, h] - ref) / max(np.linalg.norm(ref), 1e-30)
+            assert err.max() <= 2e-3 and rel <= 1e-3, (b, h, err.max(), rel)
+
+
 @pytest.mark.parametrize("cfg,kw", [
     (1, dict(steps=16)),
     (2, dict(steps=8)),
