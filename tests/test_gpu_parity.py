@@ -376,6 +376,21 @@ def test_parity_persistent_grid_at_its_graph_limit():
     run_parity(wl, fused=True)
 
 
+@pytest.mark.parametrize("per_head", [False, True], ids=["group", "per-head"])
+def test_parity_past_the_persistent_graph_limit(per_head):
+    """More graphs than the persistent attention grid takes (1280 > 1024) with a
+    list grid of several rounds: the launcher falls back to the direct grid, whose
+    empty split slots still mark their partials; group graphs of 160 ragged
+    sequences, or per-head graphs of 40."""
+    B = 40 if per_head else 160
+    _case(f"past the persistent graph limit, per_head={per_head}")
+    spec = I.ConfigSpec("many-graphs", B, 32, 8, 128, 2000, per_head, 400, 2, I.DT_BF16)
+    rng = np.random.default_rng(6)
+    wl = I.make_workload(spec, device="cuda", contexts=[int(x) for x in rng.integers(120, 2000, B)])
+    assert wl.NG == 1280
+    run_parity(wl, fused=True)
+
+
 def test_parity_persistent_grid_with_every_list_empty():
     """No sinks and a zero budget: every list is empty, the persistent grid has no
     busy split (its workers only mark the empty slots) and every output is 0."""
