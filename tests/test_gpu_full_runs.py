@@ -8,6 +8,7 @@
   long-context decoding", section "Когда CommunityKV стоит включить в план
   инфраструктуры"): the fp32 running means must stay identical on both sides
   through all of it.
+* fp32 K/V at d = 64 and bf16 at d = 64 with 8 query heads per KV head: 160 steps.
 * the 16-sequence ragged, paged workload with all 36 layers: every layer's fused
   step against the oracle, layers 0, 17 and 35 for two steps.
 * determinism: the same fused step run twice from the same state gives identical
@@ -53,6 +54,22 @@ def test_full_run_length(cfg):
     wl = I.make_workload(cfg, device="cuda")
     assert wl.steps == spec.steps
     s = run_parity(wl, fused=True, log=_every(16))
+    assert s["steps"] == spec.steps
+
+
+@pytest.mark.parametrize("spec,contexts", [
+    (I.ConfigSpec("tiny-fp32-d64-long", 2, 4, 1, 64, 2048, False, 256, 160, I.DT_F32,
+                  markov_labels=32), None),
+    (I.ConfigSpec("bf16-d64-g8-long", 2, 16, 2, 64, 6000, False, 512, 160, I.DT_BF16),
+     [6000, 2500]),
+], ids=["fp32-d64", "bf16-d64-g8"])
+def test_long_run_other_dtypes_and_shapes(spec, contexts):
+    """The long-run check in the shapes the workloads above do not have: fp32 K/V
+    at d = 64 (the tiny workload's recipe, 32 labels) and bf16 at d = 64 with 8
+    query heads per KV head, 160 decode steps each, every step compared."""
+    _case(f"{spec.name}: {spec.steps} decode steps, fused step")
+    wl = I.make_workload(spec, 59_000, device="cuda", contexts=contexts)
+    s = run_parity(wl, fused=True, log=_every(40))
     assert s["steps"] == spec.steps
 
 
